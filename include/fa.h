@@ -1,0 +1,140 @@
+/*
+ * fa.h -- C ABI of the exact, IO-aware attention library (libfa.so), gfx950.
+ *
+ * What the library computes.  For every batch entry b and head h independently
+ * (FlashAttention first principles, section 2: heads run in parallel):
+ *
+ *     S   = scale * Q K^T                          (N x N, never stored)
+ *     S_ij = -inf where key j is masked for query i
+ *     P   = softmax(S) along each row               (first principles, section 4.2)
+ *     P~  = P * Z, Z = dropout keep mask / (1 - p)  (first principles, section 2
+ *                                                    and section 3.2: dropout after softmax)
+ *     O   = P~ V
+ *     LSE_i = m_i + ln(sum_j exp(S_ij - m_i)),  m_i = max_j S_ij
+ *
+ * The forward streams K/V tiles through on-chip memory with a running row max
+ * and row sum, rescaling the partial output for every new tile, so the N x N
+ * matrix never reaches device memory (ML Canon 48 FlashAttention, "tiling and
+ * online softmax").  The backward recomputes score tiles from Q, K and the saved
+ * per-row normaliser instead of storing P (ML Canon 48 FlashAttention, "backward
+ * without N x N"; Flash Attention hardware-aware optimisation, section 2.2).
+ *
+ * Masking (element-wise, first principles section 4.1): key j is allowed for query i
+ * iff (causal == 0 || j <= i) && j < L_b, where L_b = key_lens[b] (clamped to
+ * [0, N]) or N when key_lens is NULL.  A query row with no allowed key gets
+ * O = 0, LSE = -inf and zero gradient contributions.
+ *
+ * Dropout (p > 0): element (b, h, i, j) is kept iff word (j & 3) of
+ * Philox4x32-10(counter = (j >> 2, i, h, b), key = (seed & 0xffffffff,
+ * seed >> 32)) is >= floor(p * 2^32) (p as passed, widened to double); kept
+ * values are scaled by (float)(1 / (1 - p)) computed in double.  LSE is the
+ * normaliser before dropout.  The backward must receive the forward's seed and p.
+ *
+ * Layouts.  Q, K, V, O, dO, dQ, dK, dV: contiguous [B, H, N, d], d innermost,
+ * element type `dtype`.  LSE: contiguous fp32 [B, H, N].  key_lens: device
+ * int32 [B] or NULL.  All pointers are device pointers, 16-byte aligned.
+ *
+ * Ownership.  The caller allocates and owns every buffer, including the
+ * backward workspace.  The library never allocates or frees device memory,
+ * never synchronises, and keeps no state between calls; calls on different
+ * streams may run concurrently provided their buffers do not overlap.  Outputs
+ * are overwritten, never accumulated into.  Inputs and outputs must not alias.
+ *
+ * Streams.  Every kernel is enqueued on `stream` (NULL = the default stream)
+ * and the call returns immediately; results are valid once the stream has
+ * reached that point.  Inputs must stay unchanged until then.
+ *
+ * Errors.  Arguments are checked on the host before any HIP call; on failure
+ * nothing is launched and the code says why:
+ *   FA_ERR_INVALID_ARG  NULL or misaligned pointer, B/H/N <= 0, a size whose
+ *                       element count overflows int64, non-finite or
+ *                       non-positive scale, p outside [0, 1), workspace NULL
+ *                       or smaller than fa_bwd_workspace_size().
+ *   FA_ERR_UNSUPPORTED  d not in {64, 128}; fp32 with dropout, causal masking,
+ *                       key lengths or d != 64 ... (see fa_fwd); fp32 backward.
+ *   FA_ERR_HIP          a launch failed (hipGetLastError after launching).
+ * key_lens lives in device memory and cannot be range-checked on the host; the
+ * kernels clamp each L_b into [0, N].
+ */
+#ifndef IO_AWARE_EXACT_FA_H
+#define IO_AWARE_EXACT_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_HIP = 3
+} fa_status;
+
+typedef enum {
+  FA_F32 = 0,  /* IEEE binary32 */
+  FA_BF16 = 1  /* bfloat16, round-to-nearest-even on output */
+} fa_dtype;
+
+/*
+ * Forward pass: O and LSE.
+ *
+ *   q, k, v   [B, H, N, d] of dtype, read only.
+ *   o         [B, H, N, d] of dtype, written.
+ *   lse       [B, H, N] fp32, written (natural log, scaled-score units).
+ *   scale     multiplier of Q K^T (1/sqrt(d) for standard attention,
+ *             ML Canon 48 FlashAttention, the PyTorch SDPA box).
+ *   causal    non-zero: key j is masked for query i when j > i (top-left).
+ *   key_lens  device int32 [B] or NULL (all keys valid).
+ *   dropout_p probability of dropping an element, 0 <= p < 1.
+ *   seed      Philox key, used only when dropout_p > 0.
+ *
+ * dtype FA_BF16: d in {64, 128}, every mask and dropout combination.
+ * dtype FA_F32:  d == 64, no causal mask, no key_lens, no dropout
+ *                (the single-head fp32 workload); anything else returns
+ *                FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                 const int32_t* key_lens, float dropout_p, uint64_t seed,
+                 hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes: an fp32 [B, H, N, d]
+ * dQ accumulator followed by the fp32 [B, H, N] row terms D_i = sum_k dO_ik O_ik.
+ * Returns 0 for arguments fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype);
+
+/*
+ * Backward pass: dQ, dK, dV for upstream gradient dout, recomputing the score
+ * tiles from q, k and the forward's lse.
+ *
+ *   q, k, v, o, dout  [B, H, N, d] of dtype, read only (o and lse from fa_fwd
+ *                     with the same scale, causal, key_lens, dropout_p, seed).
+ *   lse               [B, H, N] fp32, read only.
+ *   dq, dk, dv        [B, H, N, d] of dtype, written.
+ *   workspace         device buffer of at least fa_bwd_workspace_size() bytes,
+ *                     16-byte aligned; its contents on entry do not matter and
+ *                     are garbage on exit.
+ *
+ * dtype FA_BF16 only (d in {64, 128}).  dK and dV are bitwise deterministic;
+ * dQ is accumulated with fp32 atomics, so its last bits may vary between runs.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                 int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                 const int32_t* key_lens, float dropout_p, uint64_t seed,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* fa_status_string(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IO_AWARE_EXACT_FA_H */
