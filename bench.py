@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark: attention forward + backward TFLOP/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is the whole hot path on the causal decoder workload (B=4, H=32,
+N=4096, d=128, bf16, i.i.d. N(0,1) inputs drawn from a fixed seed): one fa_fwd
+(O and LSE) followed by one fa_bwd (D preprocess, recompute backward, dQ
+convert), inputs resident in device memory.  W untimed steps, then exactly K
+timed steps between device synchronisations.  Prints one JSON line.
+
+FLOP convention (causal halves the work): forward 4*B*H*N^2*d/2, backward 2.5x
+the forward (five N x N x d products including the recomputed Q K^T).
+Roofline peak: MI355X dense bf16 MFMA, 2500 TFLOP/s (published).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+WORKLOAD_NUMBER = 3
+
+
+def flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+    return f, 2.5 * f
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "io_aware_exact_24_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=30.0):
+    """The oracle, untouched, on one head of the workload (fwd + bwd), timed on
+    the host cores; scaled to the metric's unit (algorithmic TFLOP/s)."""
+    import numpy as np
+
+    from io_aware_exact_24_amd.workloads import draw
+    from oracle import attention_backward, attention_forward
+
+    inp = draw(1, 1, w.N, w.d, w.torch_dtype, seed=w.seed)
+    t0 = time.perf_counter()
+    attention_forward(inp.q, inp.k, inp.v, w.scale, w.causal)
+    attention_backward(inp.q, inp.k, inp.v, inp.dout, w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    ff, fb = flops(1, 1, w.N, w.d, w.causal)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {
+        "value": (ff + fb) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": min(cores, threads),
+        "kind": "oracle",
+        "sample": f"one head (B=1, H=1) of the workload, forward + backward, fp64 numpy, "
+                  f"{dt:.1f} s wall",
+        "seconds": dt,
+        "numpy_blas_threads_hint": threads,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("this benchmark runs on exactly one GPU (the attention path has no multi-GPU "
+              "component here); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from io_aware_exact_24_amd import binding
+    from io_aware_exact_24_amd.workloads import WORKLOADS, draw_workload
+
+    w = WORKLOADS[WORKLOAD_NUMBER]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = draw_workload(w)
+    q, k, v, do = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.dout))
+    B, H, N, d = w.B, w.H, w.N, w.d
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(binding.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, 0.0, 0, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        binding.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.scale, w.causal, None, 0.0, 0, ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
+    bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in events)
+    avg_fwd = sum(fwd_ms) / len(fwd_ms)
+    avg_bwd = sum(bwd_ms) / len(bwd_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    ff, fb = flops(B, H, N, d, w.causal)
+    fwd_tf = ff / (avg_fwd * 1e-3) / 1e12
+    bwd_tf = fb / (avg_bwd * 1e-3) / 1e12
+    value = (ff + fb) / (ms_per_step * 1e-3) / 1e12
+
+    # Dominant kernel: the backward (2.5x the forward's work).  Its launch time
+    # is the whole fa_bwd call (D preprocess + main + dQ convert) between HIP
+    # events on the library's stream, so the achieved rate is a lower bound for
+    # the main kernel alone.
+    dom, dom_ms, dom_flops = ("bwd_main", avg_bwd, fb) if avg_bwd >= avg_fwd else ("fwd", avg_fwd, ff)
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "kernel": dom,
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": stored_traffic(dom),
+        "launch_ms": round(dom_ms, 4),
+        "flop_per_launch": dom_flops,
+    }
+    rec = {
+        "metric": "attention fwd/bwd TFLOP/s at N=4096,d=128 causal bf16; % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decoder_causal: B=4 H=32 N=4096 d=128 causal bf16, N(0,1) inputs",
+                   "B": B, "H": H, "N": N, "d": d, "causal": True, "dropout_p": 0.0},
+        "fwd": {"ms": round(avg_fwd, 4), "tflops": round(fwd_tf, 2),
+                "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(avg_bwd, 4), "tflops": round(bwd_tf, 2),
+                "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,4 +15,6 @@ from .binding import (  # noqa: F401
     fa_status_string,
     library_path,
     load_library,
+    forward,
+    backward,
 )

@@ -1,0 +1,168 @@
+"""ctypes binding of libfa.so with the C ABI's entry-point names.
+
+Argument marshalling only: torch tensors are checked for shape, dtype, device
+and contiguity, then passed as raw device pointers together with the HIP
+stream handle of torch's current stream.  All compute happens in the
+library's kernels.  If libfa.so is missing the first call raises; there is no
+fallback.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libfa.so"
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F32, FA_BF16 = 0, 1
+
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {fa_status_string(status)} (status {status})")
+
+
+def library_path():
+    return os.path.join(PKG, LIB_NAME)
+
+
+def load_library():
+    """Load libfa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise OSError(f"{path} is missing; build it with `python -m io_aware_exact_24_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, u64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_size_t
+    lib.fa_fwd.restype = i
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64,
+                           vp, sz, vp]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [i]
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status):
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, shape, dtype, device, name):
+    if t.shape != shape or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {tuple(shape)} {dtype} on {device}, got "
+                         f"{tuple(t.shape)} {t.dtype} on {t.device} (contiguous={t.is_contiguous()})")
+
+
+def _stream(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _key_lens(key_lens, B, device):
+    import torch
+
+    if key_lens is None:
+        return None
+    _check(key_lens, (B,), torch.int32, device, "key_lens")
+    return key_lens
+
+
+def fa_fwd(q, k, v, o, lse, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
+           stream=None):
+    """Enqueue the forward pass; o and lse are written.  See include/fa.h."""
+    import torch
+
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        _check(t, q.shape, q.dtype, q.device, name)
+    _check(q, q.shape, q.dtype, q.device, "q")
+    _check(lse, (B, H, N), torch.float32, q.device, "lse")
+    kl = _key_lens(key_lens, B, q.device)
+    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _dtype_code(q),
+                    float(scale), int(bool(causal)), _ptr(kl), float(dropout_p), int(seed),
+                    _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+
+
+def fa_bwd_workspace_size(B, H, N, d, dtype_code=FA_BF16):
+    return int(load_library().fa_bwd_workspace_size(B, H, N, d, dtype_code))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None,
+           dropout_p=0.0, seed=0, workspace=None, stream=None):
+    """Enqueue the backward pass; dq, dk, dv are written.  workspace: a uint8
+    device tensor of at least fa_bwd_workspace_size() bytes."""
+    import torch
+
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, q.shape, q.dtype, q.device, name)
+    _check(q, q.shape, q.dtype, q.device, "q")
+    _check(lse, (B, H, N), torch.float32, q.device, "lse")
+    kl = _key_lens(key_lens, B, q.device)
+    if workspace is None:
+        raise ValueError("fa_bwd needs a workspace tensor (see fa_bwd_workspace_size)")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                    _ptr(dv), B, H, N, d, _dtype_code(q), float(scale), int(bool(causal)), _ptr(kl),
+                    float(dropout_p), int(seed), _ptr(workspace), ws_bytes,
+                    _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+
+
+def forward(q, k, v, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0, stream=None):
+    """Allocate O and LSE with torch and call fa_fwd."""
+    import torch
+
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal, key_lens, dropout_p, seed, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, dout, lse, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
+             stream=None, workspace=None):
+    """Allocate dQ, dK, dV (and the workspace unless given) and call fa_bwd."""
+    import torch
+
+    B, H, N, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    if workspace is None:
+        nbytes = fa_bwd_workspace_size(B, H, N, d, _dtype_code(q))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, key_lens, dropout_p, seed,
+           workspace, stream)
+    return dq, dk, dv

@@ -1,0 +1,137 @@
+// C ABI of libfa.so: argument checks (all on the host, before any HIP call),
+// workspace sizing, and dispatch to the gfx950 kernel launchers.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+// Element count of one [B, H, N, d] tensor, or -1 when it would overflow int64
+// or the per-kernel 32-bit index ranges (rows B*H*N must fit in int32).
+int64_t elems(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return -1;
+  const int64_t rows = (int64_t)B * H * N;
+  if (rows > INT32_MAX) return -1;
+  const int64_t n = rows * d;
+  if (n / d != rows) return -1;
+  return n;
+}
+
+bool valid_dropout(float p) { return isfinite(p) && p >= 0.0f && p < 1.0f; }
+
+uint32_t drop_threshold(float p) {
+  // floor(p * 2^32) in double; p < 1 keeps it below 2^32.
+  return (uint32_t)floor((double)p * 4294967296.0);
+}
+
+float drop_scale(float p) { return (float)(1.0 / (1.0 - (double)p)); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, fa_dtype dtype, float scale, int causal, const int32_t* key_lens,
+                 float dropout_p, uint64_t seed, hipStream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if (key_lens != nullptr && ((uintptr_t)key_lens & 3u) != 0) return FA_ERR_INVALID_ARG;
+  if (elems(B, H, N, d) < 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale <= 0.0f) return FA_ERR_INVALID_ARG;
+  if (!valid_dropout(dropout_p)) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32 && dropout_p > 0.0f) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.key_lens = key_lens;
+  a.dropout_p = dropout_p;
+  a.drop_threshold = drop_threshold(dropout_p);
+  a.drop_scale = drop_scale(dropout_p);
+  a.seed = seed;
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, stream) : fa::launch_fwd_f32(a, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype) {
+  if (dtype != FA_BF16 || (d != 64 && d != 128)) return 0;
+  const int64_t n = elems(B, H, N, d);
+  if (n < 0) return 0;
+  const int64_t rows = (int64_t)B * H * N;
+  // fp32 dQ accumulator, then fp32 D, each rounded up to 256 bytes.
+  const size_t acc = ((size_t)n * 4 + 255) & ~(size_t)255;
+  const size_t dl = ((size_t)rows * 4 + 255) & ~(size_t)255;
+  return acc + dl;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                 fa_dtype dtype, float scale, int causal, const int32_t* key_lens, float dropout_p,
+                 uint64_t seed, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_INVALID_ARG;
+  if (key_lens != nullptr && ((uintptr_t)key_lens & 3u) != 0) return FA_ERR_INVALID_ARG;
+  const int64_t n = elems(B, H, N, d);
+  if (n < 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale <= 0.0f) return FA_ERR_INVALID_ARG;
+  if (!valid_dropout(dropout_p)) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d, dtype);
+  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.key_lens = key_lens;
+  a.dropout_p = dropout_p;
+  a.drop_threshold = drop_threshold(dropout_p);
+  a.drop_scale = drop_scale(dropout_p);
+  a.seed = seed;
+  a.dq_acc = (float*)workspace;
+  a.delta = (float*)((char*)workspace + (((size_t)n * 4 + 255) & ~(size_t)255));
+  const hipError_t e = fa::launch_bwd_bf16(a, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Device-side building blocks shared by the gfx950 attention kernels:
+// vector types, the MFMA and LDS-transpose intrinsics, lane exchange across the
+// two 32-lane halves of a wave, and the Philox4x32-10 generator that draws the
+// dropout keep mask.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16).  Lane l supplies row/column
+// (l % 32) of A/B and eight consecutive k-slots 8*(l/32) .. 8*(l/32)+7; the
+// result register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transposing read of four 16-bit elements.  Within each group of 16 lanes,
+// lane t receives element (t % 4) of the 8-byte load issued by lane 4*e + t/4 as
+// its element e.  If lane s of the group points at row (s / 4) and column
+// 4*(s % 4) of a row-major 4 x 16 block, lane t therefore gets column t of the
+// block: the four rows' values of that column.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* lds_ptr) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)((uintptr_t)lds_ptr)));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Value held by lane (l ^ 32): the two halves of the wave swap.
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // r[0]: lanes 0-31 keep their own value, lanes 32-63 get lane l-32's;
+  // r[1]: lanes 0-31 get lane l+32's, lanes 32-63 keep their own.
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// max and sum over the lane pair (l, l ^ 32); both lanes get the same bits.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);  // lower lane's value first in both
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds of
+//   (c0, c1, c2, c3) -> (hi(B*c2) ^ c1 ^ k0, lo(B*c2), hi(A*c0) ^ c3 ^ k1, lo(A*c0))
+// with A = 0xD2511F53, B = 0xCD9E8D57, the key advanced by the Weyl increments
+// (0x9E3779B9, 0xBB67AE85) between rounds.
+__device__ __forceinline__ u32x4 philox(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                        uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  u32x4 out = {c0, c1, c2, c3};
+  return out;
+}
+
+// Remap a linear workgroup id so that consecutive logical ids run on the same
+// XCD.  The dispatcher deals workgroups round-robin to the 8 XCDs, so physical
+// id p lands on XCD p % 8; logical id (p % 8) * (G / 8) + p / 8 puts each XCD's
+// share in one contiguous logical range.  Only applied when G % 8 == 0.
+__device__ __forceinline__ int xcd_remap(int p, int G) {
+  if ((G & 7) != 0) return p;
+  return (p & 7) * (G >> 3) + (p >> 3);
+}
+
+}  // namespace fa

@@ -1,0 +1,53 @@
+// Host-side argument bundles passed from the C ABI layer to the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  const int32_t* key_lens;  // device [B] or nullptr
+  float dropout_p;          // 0 disables dropout
+  uint32_t drop_threshold;  // floor(p * 2^32)
+  float drop_scale;         // fp32(1 / (1 - p))
+  uint64_t seed;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  const int32_t* key_lens;
+  float dropout_p;
+  uint32_t drop_threshold;
+  float drop_scale;
+  uint64_t seed;
+  float* dq_acc;  // workspace: fp32 [B, H, N, d]
+  float* delta;   // workspace: fp32 [B, H, N]
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+
+}  // namespace fa

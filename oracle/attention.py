@@ -101,11 +101,12 @@ def _row_groups(n, rows, row_chunk):
 
 
 def attention_forward(q, k, v, scale, causal=False, key_lens=None, dropout_p=0.0,
-                      seed=0, rows=None, row_chunk=None):
+                      seed=0, rows=None, row_chunk=None, heads=None):
     """O and LSE of the attention definition, in fp64.
 
     q, k, v: [B, H, N, d] (numpy or torch, any float dtype; widened exactly).
     key_lens: None or length-B integers.  rows: optional query rows to evaluate.
+    heads: optional list of (b, h) pairs to evaluate (others are left zero).
     Returns (O [B, H, R, d], LSE [B, H, R]) with R = N or len(rows).
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
@@ -113,29 +114,32 @@ def attention_forward(q, k, v, scale, causal=False, key_lens=None, dropout_p=0.0
     nrows = N if rows is None else len(rows)
     out = np.zeros((B, H, nrows, d))
     lse = np.zeros((B, H, nrows))
-    for b in range(B):
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
         L = N if key_lens is None else int(key_lens[b])
-        for h in range(H):
-            pos = 0
-            for grp in _row_groups(N, rows, row_chunk):
-                p, l = _head_probs(q[b, h, grp], k[b, h], scale, grp, causal, L)
-                z = _head_z(seed, b, h, grp, N, dropout_p)
-                pt = p if z is None else p * z
-                out[b, h, pos : pos + len(grp)] = pt @ v[b, h]
-                lse[b, h, pos : pos + len(grp)] = l
-                pos += len(grp)
+        pos = 0
+        for grp in _row_groups(N, rows, row_chunk):
+            p, l = _head_probs(q[b, h, grp], k[b, h], scale, grp, causal, L)
+            z = _head_z(seed, b, h, grp, N, dropout_p)
+            pt = p if z is None else p * z
+            out[b, h, pos : pos + len(grp)] = pt @ v[b, h]
+            lse[b, h, pos : pos + len(grp)] = l
+            pos += len(grp)
     return out, lse
 
 
 def attention_backward(q, k, v, dout, scale, causal=False, key_lens=None,
                        dropout_p=0.0, seed=0, q_rows=None, k_rows=None,
-                       row_chunk=None, heads=None):
+                       row_chunk=None, heads=None, first_row=0):
     """dQ, dK, dV of the attention definition for upstream gradient dout, in fp64.
 
     q_rows selects the rows of dQ that are returned, k_rows the rows of dK and
     dV (all by default).  Every query row takes part in dK and dV, so all rows
     are evaluated unless k_rows is empty, in which case only q_rows are.
     heads: optional list of (b, h) pairs to evaluate (others are left zero).
+    first_row: with a causal mask, query rows below min(k_rows) never see those
+    keys, so only rows >= first_row need evaluating for dK/dV (exact when
+    first_row <= min(k_rows); requires causal and explicit k_rows).
     Returns (dQ [B, H, Rq, d], dK [B, H, Rk, d], dV [B, H, Rk, d]).
     """
     q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
@@ -150,6 +154,10 @@ def attention_backward(q, k, v, dout, scale, causal=False, key_lens=None,
         L = N if key_lens is None else int(key_lens[b])
         dq_full = np.zeros((N, d)) if q_rows is None else None
         eval_rows = q_sel if len(k_sel) == 0 else None
+        if first_row > 0:
+            if not causal or k_rows is None or q_rows is None or first_row > int(np.min(k_sel)):
+                raise ValueError("first_row needs causal masking, explicit q_rows and k_rows >= first_row")
+            eval_rows = np.union1d(np.arange(first_row, N), q_sel)
         for grp in _row_groups(N, eval_rows, row_chunk):
             p, _ = _head_probs(q[b, h, grp], k[b, h], scale, grp, causal, L)
             z = _head_z(seed, b, h, grp, N, dropout_p)

@@ -1,0 +1,113 @@
+"""C-ABI checks that run without a GPU.
+
+libfa.so must load, export every function include/fa.h declares, and reject
+bad arguments on the host before any HIP call (so the error paths can be
+exercised here with dummy, never-dereferenced pointers).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from io_aware_exact_24_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, INVALID, UNSUPPORTED = binding.FA_OK, binding.FA_ERR_INVALID_ARG, binding.FA_ERR_UNSUPPORTED
+P = 0x10000  # a 16-byte-aligned dummy address; validation fails before it is used
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        pytest.fail("libfa.so is not built (python -m io_aware_exact_24_amd.build)")
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings(lib):
+    assert binding.fa_status_string(OK) == "ok"
+    assert binding.fa_status_string(INVALID) == "invalid argument"
+    assert binding.fa_status_string(UNSUPPORTED) == "unsupported configuration"
+    assert binding.fa_status_string(binding.FA_ERR_HIP) == "HIP launch error"
+    assert binding.fa_status_string(42) == "unknown status"
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16,
+        scale=0.125, causal=0, key_lens=None, p=0.0, seed=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, key_lens, p, seed, None)
+
+
+def bwd(lib, ptrs=None, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, scale=0.125, causal=0,
+        key_lens=None, p=0.0, seed=0, ws=P, ws_bytes=None):
+    ptrs = ptrs or [P] * 9
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d, dtype)
+    return lib.fa_bwd(*ptrs, B, H, N, d, dtype, scale, causal, key_lens, p, seed, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(lse=None), INVALID),
+    (dict(k=P + 8), INVALID), (dict(v=P + 4), INVALID), (dict(key_lens=P + 2), INVALID),
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID),
+    (dict(B=1 << 16, H=1 << 16, N=1), INVALID),            # B*H*N overflows int32 rows
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(p=1.0), INVALID), (dict(p=-0.1), INVALID), (dict(p=float("nan")), INVALID),
+    (dict(dtype=7), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(dtype=binding.FA_F32, p=0.1), UNSUPPORTED),
+])
+def test_forward_rejects(lib, kw, expect):
+    assert fwd(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=0), INVALID), (dict(scale=float("nan")), INVALID), (dict(p=1.0), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(dtype=binding.FA_F32), UNSUPPORTED),
+    (dict(ws=None), INVALID), (dict(ws=P + 4), INVALID), (dict(ws_bytes=0), INVALID),
+])
+def test_backward_rejects(lib, kw, expect):
+    assert bwd(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("idx", range(9))
+def test_backward_rejects_null_tensor(lib, idx):
+    ptrs = [P] * 9
+    ptrs[idx] = None
+    assert bwd(lib, ptrs=ptrs) == INVALID
+
+
+def test_backward_rejects_short_workspace(lib):
+    need = lib.fa_bwd_workspace_size(2, 3, 100, 128, binding.FA_BF16)
+    assert bwd(lib, B=2, H=3, N=100, d=128, ws_bytes=need - 1) == INVALID
+
+
+def test_workspace_size_is_linear_in_n():
+    # fp32 dQ accumulator plus fp32 D, each padded to 256 bytes: O(B*H*N*d), never O(N^2).
+    ws = binding.fa_bwd_workspace_size
+    assert ws(1, 1, 128, 64) == 128 * 64 * 4 + 512
+    assert ws(4, 32, 4096, 128) == 4 * 32 * 4096 * 128 * 4 + 4 * 32 * 4096 * 4
+    assert ws(1, 8, 65536, 64) == 8 * 65536 * 64 * 4 + 8 * 65536 * 4
+    assert ws(1, 1, 65536, 64) < 65536 * 65536 // 16
+    assert ws(1, 1, 128, 96) == 0
+    assert ws(1, 1, 128, 64, binding.FA_F32) == 0
+    assert ws(0, 1, 128, 64) == 0

@@ -135,3 +135,17 @@ def test_preprocess_term_equals_jacobian_contraction():
     dp = do[0, 0] @ v[0, 0].T
     np.testing.assert_allclose(backward_preprocess(o, do)[0, 0], np.sum(p[0, 0] * dp, axis=1),
                                atol=1e-13)
+
+
+def test_first_row_restriction_is_exact_for_causal():
+    B, H, N, d = 1, 1, 40, 4
+    q, k, v, do = rand(B, H, N, d), rand(B, H, N, d), rand(B, H, N, d), rand(B, H, N, d)
+    kw = dict(scale=0.6, causal=True)
+    dq, dk, dv = attention_backward(q, k, v, do, **kw)
+    keys, rows = np.array([25, 30, 39]), np.array([3, 26])
+    dq2, dk2, dv2 = attention_backward(q, k, v, do, q_rows=rows, k_rows=keys, first_row=25, **kw)
+    np.testing.assert_allclose(dk2, dk[:, :, keys], atol=1e-13)
+    np.testing.assert_allclose(dv2, dv[:, :, keys], atol=1e-13)
+    np.testing.assert_allclose(dq2, dq[:, :, rows], atol=1e-13)
+    with pytest.raises(ValueError):
+        attention_backward(q, k, v, do, q_rows=rows, k_rows=keys, first_row=26, **kw)
