@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("this benchmark runs on exactly one GPU (the attention path has no multi-GPU "
@@ -114,6 +116,15 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     ws = torch.empty(binding.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.calibrate_copy:
+        # A plain copy of known size: reads 256 MiB and writes 256 MiB, so the
+        # HBM byte counters of this kernel give their scale against true bytes.
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         if ev is not None:
