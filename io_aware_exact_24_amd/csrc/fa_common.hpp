@@ -39,6 +39,19 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* lds_ptr) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// LDS-typed pointers: arithmetic on them stays visible to the backend, which
+// folds constant displacements into the 16-bit offset field of the DS
+// instruction instead of materialising one address register per access.
+typedef __attribute__((address_space(3))) bf16 lds_bf16;
+__device__ __forceinline__ const lds_bf16* to_lds(const bf16* p) {
+  return (const lds_bf16*)p;
+}
+__device__ __forceinline__ bf16x4 lds_read_tr4(const lds_bf16* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
 // Value held by lane (l ^ 32): the two halves of the wave swap.
 __device__ __forceinline__ float other_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -91,5 +104,28 @@ __device__ __forceinline__ int xcd_remap(int p, int G) {
   if ((G & 7) != 0) return p;
   return (p & 7) * (G >> 3) + (p >> 3);
 }
+
+
+// Buffer resource for raw byte-addressed loads from [base, base + bytes).  A
+// load whose 16-byte range lies past `bytes` returns zeros, which gives the
+// ragged tail of a sequence for free.  The last word selects 32-bit raw
+// buffer access on gfx9-family parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's 16 bytes from
+// byte offset `voff` of the buffer land at LDS byte address
+// lds_wave_base + 16 * l (lds_wave_base is the same for the whole wave).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, const void* lds_wave_base,
+                                          uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory loads (including LDS DMA)
+// have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace fa

@@ -3,20 +3,34 @@
 // O = softmax(mask(scale * Q K^T)) (with dropout) V and the per-row
 // LSE = m + ln(l), computed tile by tile: each workgroup keeps a block of
 // queries resident, streams K/V tiles through LDS, and keeps a running row max
-// m and row sum l, rescaling the partial output whenever m grows (ML Canon 48
+// m and row sum l, rescaling the partial output when m grows (ML Canon 48
 // FlashAttention, "tiling and online softmax").  The N x N scores exist only as
 // one register tile at a time (FlashAttention first principles, section 4.2, explains
 // why the row-wise softmax otherwise forces them into device memory).
 //
-// bf16 path.  Each wave owns 32 queries and computes the transposed score tile
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so every lane holds the scores of
-// ONE query against 16 keys of each 32-key block (its partner lane l^32 holds
-// the other 16).  That orientation makes
-//   * the row max/sum a per-lane reduction plus one permlane32 swap,
-//   * the rescale factor a per-lane scalar for the transposed output O^T,
-//   * the probabilities, converted to bf16, exactly the B operand of the next
-//     MFMA O^T += V^T P^T with no data movement,
-// while V^T is read from the row-major V tile with the LDS transposing read.
+// bf16 path, per workgroup of 4 waves x 32 queries, two workgroups per CU:
+//  * Each wave computes the transposed score tile S^T = K Q^T with
+//    v_mfma_f32_32x32x16_bf16: Q^T is the B operand held in registers for the
+//    whole loop, K rows the A operand read from LDS.  In that layout a lane
+//    holds the scores of ONE query against 16 keys of each 32-key block (its
+//    partner lane l^32 the other 16), so the row max/sum is a per-lane
+//    reduction plus one permlane32 swap, and the probabilities, converted to
+//    bf16, are already the B operand of O^T += V^T P^T.  V^T comes from the
+//    row-major V tile through the LDS transposing read.
+//  * K and V tiles (64 keys) are copied global -> LDS directly by buffer loads
+//    (no register staging), double buffered, with an XOR swizzle of the
+//    16-byte chunks of each row that keeps both the row reads of K and the
+//    transposing reads of V free of bank conflicts.  Rows past N read as zero.
+//  * Software pipeline: while the MFMAs of the next tile's scores run, the
+//    VALU works on the current tile's exponentials; the next tile's row max is
+//    taken while the P V products run.
+//  * Lazy rescaling: the reference max used in the exponent only moves when a
+//    row max exceeds it by more than 2^8 (in base-2 units), so the rescale of
+//    the output accumulator is a rare, wave-uniform branch.  Numerators and
+//    the denominator always use the same reference, so the result is the same
+//    softmax; probabilities stay below 2^8 before normalisation.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 
@@ -39,24 +53,47 @@ struct FwdParams {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int NW = 8;                    // waves per workgroup
+  static constexpr int NW = 4;                  // waves per workgroup
   static constexpr int THREADS = NW * 64;
-  static constexpr int BM = 32 * NW;              // queries per workgroup
-  static constexpr int BN = 64;                   // keys per K/V tile
-  static constexpr int KP = D + 8;                // K tile row pitch (elements)
-  static constexpr int VP = D + 32;               // V tile row pitch (elements)
-  static constexpr int K_ELEMS = BN * KP;
-  static constexpr int STAGE = BN * KP + BN * VP;  // one K tile + one V tile
-  static constexpr int ROW_CHUNKS = D / 8;        // 16-byte chunks per row
-  static constexpr int CPT = BN * ROW_CHUNKS / THREADS;  // chunks per thread per tile
-  static_assert(CPT >= 1 && CPT * THREADS == BN * ROW_CHUNKS, "tile/thread mismatch");
+  static constexpr int BM = 32 * NW;            // queries per workgroup
+  static constexpr int BN = 64;                 // keys per K/V tile
+  static constexpr int CHUNKS = D / 8;          // 16-byte chunks per row
+  static constexpr int TILE = BN * D;           // elements per K or V tile
+  static constexpr int LOADS = BN * CHUNKS / THREADS;  // 16-byte copies per thread per tile
+  static_assert(LOADS * THREADS == BN * CHUNKS, "tile/thread mismatch");
 };
 
+// Physical 16-byte chunk slot of logical chunk c in tile row r is c ^ swz(r).
+// d = 128 (16 chunks, 256-byte rows): 16 consecutive rows get 16 distinct
+// values (row reads of 16 lanes hit all 64 banks once) and 4 aligned
+// consecutive rows differ in bits 2-3 (the transposing read of 4 rows x 64
+// bytes hits 4 different 64-byte bank groups).  d = 64 (8 chunks, 128-byte
+// rows): the same two properties with two rows per 256-byte bank cycle.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+}
+
 template <int D, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_bf16_kernel(FwdParams p) {
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_kernel(FwdParams p) {
   using C = FwdCfg<D>;
-  constexpr int BN = C::BN, KP = C::KP, VP = C::VP;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+  constexpr int BN = C::BN, NW = C::NW, TILE = C::TILE;
+  constexpr int KC = D / 16;  // MFMA k-steps over the head dimension
+  constexpr int DU = D / 32;  // 32-wide blocks of the head dimension
+  // K and V tiles, two stages each.  Separate objects let the compiler see
+  // that a copy into one stage cannot alias reads of another, so it does not
+  // make those reads wait for the copy.
+  __shared__ __attribute__((aligned(1024))) bf16 sk0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sk1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sv0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sv1[TILE];
+  auto kbuf = [&](int stage) -> bf16* { return stage ? sk1 : sk0; };
+  auto vbuf = [&](int stage) -> bf16* { return stage ? sv1 : sv0; };
 
   const int N = p.N;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -73,16 +110,20 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_bf16_kernel(FwdPara
   if (p.key_lens) L = min(max(p.key_lens[bi], 0), N);
   const int kend = CAUSAL ? min(L, q0 + C::BM) : L;  // keys [0, kend) matter to the workgroup
   const int nkb = (kend + BN - 1) / BN;
+  // Tiles [0, nfree) are unmasked for every query of the workgroup.
+  int nfree = L / BN;
+  if (CAUSAL) nfree = min(nfree, q0 / BN);
+  nfree = min(nfree, nkb);
 
   const size_t head_off = (size_t)head * N * D;
   const bf16* __restrict__ qg = p.q + head_off;
-  const bf16* __restrict__ kg = p.k + head_off;
-  const bf16* __restrict__ vg = p.v + head_off;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, (uint32_t)N * D * 2);
 
   // Q^T as the B operand of S^T = K Q^T: lane holds Q[qi][16c + 8hh .. +7].
-  bf16x8 qreg[D / 16];
+  bf16x8 qreg[KC];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
+  for (int c = 0; c < KC; ++c) {
     if (qi < N) {
       qreg[c] = *(const bf16x8*)(qg + (size_t)qi * D + 16 * c + 8 * hh);
     } else {
@@ -91,165 +132,248 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_bf16_kernel(FwdPara
     }
   }
 
-  f32x16 oacc[D / 32];
+  // Per-lane byte offsets of this thread's 16-byte copies within a tile.
+  uint32_t ld_off[C::LOADS];
 #pragma unroll
-  for (int u = 0; u < D / 32; ++u)
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int pch = (i * NW + wave) * 64 + lane;  // physical chunk slot written by this lane
+    const int r = pch / C::CHUNKS, pc = pch % C::CHUNKS;
+    ld_off[i] = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
+  }
+  auto issue_k = [&](int jt, int stage) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+      lds_dma16(krs, kbuf(stage) + (i * NW + wave) * 512, ld_off[i] + (uint32_t)jt * (BN * D * 2));
+  };
+  auto issue_v = [&](int jt, int stage) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+      lds_dma16(vrs, vbuf(stage) + (i * NW + wave) * 512,
+                ld_off[i] + (uint32_t)jt * (BN * D * 2));
+  };
+
+  // LDS element offsets of the MFMA operand reads (stage 0; stage 1 adds TILE).
+  // K rows: row 32t + li, logical chunk 2c + hh.
+  const int ksw = swz<D>(li);
+  int koff[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) koff[c] = li * D + (((2 * c + hh) ^ ksw) * 8);
+  // V^T by transposing reads: rows 16cc + trow (+8), logical columns 32u + tcol.
+  const int g16 = lane & 15;
+  const int trow = 4 * hh + (g16 >> 2);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+  int voff[2][DU];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      const int r = trow + 8 * half;
+      voff[half][u] = r * D + (((4 * u + (tcol >> 3)) ^ swz<D>(r)) * 8) + (tcol & 7);
+    }
+
+  f32x16 oacc[DU];
+#pragma unroll
+  for (int u = 0; u < DU; ++u)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[u][r] = 0.0f;
-  float m = -INFINITY;  // running max of raw scores (q.k) for query qi
-  float l = 0.0f;       // this lane's partial row sum (its 16 keys of every 32)
-
   const float c2 = p.scale_log2;
+  float mref = -INFINITY;  // reference max of this query row, in scale*log2 units
+  float l = 0.0f;          // this lane's partial row sum (its 16 keys of every 32)
 
-  // Global -> register staging of one K/V tile; rows past N read as zero.
-  uint4 kreg[C::CPT], vreg[C::CPT];
-  auto load_tile = [&](int jb) {
+  auto qk = [&](int stage, f32x16 (&s)[2]) {
+    const bf16* ks = kbuf(stage);
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + i * C::THREADS;
-      const int row = jb * BN + c / C::ROW_CHUNKS;
-      const int col = (c % C::ROW_CHUNKS) * 8;
-      if (row < N) {
-        kreg[i] = *(const uint4*)(kg + (size_t)row * D + col);
-        vreg[i] = *(const uint4*)(vg + (size_t)row * D + col);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const bf16x8 a = *(const bf16x8*)(ks + koff[c] + t * 32 * D);
+        s[t] = mfma32(a, qreg[c], s[t]);
       }
     }
   };
-  auto store_tile = [&](int stage) {
-    bf16* ks = smem + stage * C::STAGE;
-    bf16* vs = ks + C::K_ELEMS;
+  auto apply_mask = [&](int jt, f32x16 (&s)[2]) {
+    // key = kb + key_of(t, r) with kb per lane; allowed iff key_of(t, r) < lim.
+    const int kb = jt * BN + 4 * hh;
+    int lim = L - kb;
+    if (CAUSAL) lim = min(lim, qi - kb + 1);
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + i * C::THREADS;
-      const int row = c / C::ROW_CHUNKS;
-      const int col = (c % C::ROW_CHUNKS) * 8;
-      *(uint4*)(ks + row * KP + col) = kreg[i];
-      *(uint4*)(vs + row * VP + col) = vreg[i];
-    }
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kc = 32 * t + 8 * (r >> 2) + (r & 3);
+        s[t][r] = kc < lim ? s[t][r] : -INFINITY;
+      }
   };
-
-  if (nkb > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int jb = 0; jb < nkb; ++jb) {
-    const int cur = jb & 1;
-    if (jb + 1 < nkb) load_tile(jb + 1);
-    const int kb = jb * BN;
-    const bool active = (!CAUSAL || kb <= qw + 31) && qw < N;
-    if (active) {
-      const bf16* ks = smem + cur * C::STAGE;
-      const bf16* vs = ks + C::K_ELEMS;
-
-      // S^T tile (64 keys x 32 queries) as two 32x32 MFMA tiles.
-      f32x16 s[2];
+  // Row max of a tile (both partner lanes get it), scaled to exp2 units, and
+  // the wave-uniform decision whether the reference max must move.
+  auto tile_max = [&](const f32x16 (&s)[2]) {
+    float mx = s[0][0];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+      for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    return pair_max(mx) * c2;
+  };
+  auto rescale_if_needed = [&](float mxc) {
+    const bool grow = mxc > mref + 8.0f;
+    if (__ballot(grow) != 0) {
+      const float mnew = fmaxf(mref, mxc);
+      const float alpha = mnew == -INFINITY ? 1.0f : fast_exp2(mref - mnew);
+      mref = mnew;
+      l *= alpha;
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const bf16x8 a = *(const bf16x8*)(ks + (32 * t + li) * KP + 16 * c + 8 * hh);
-          s[t] = mfma32(a, qreg[c], s[t]);
-        }
-      }
-
-      // Mask: padding / tail keys and, for causal, keys after the query.
-      const bool need_mask = (kb + BN > L) || (CAUSAL && kb + BN - 1 > qw);
-      if (need_mask) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = key < L && (!CAUSAL || key <= qi);
-            s[t][r] = ok ? s[t][r] : -INFINITY;
-          }
-      }
-
-      // Online softmax update.
-      float mx = s[0][0];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float ms = m_use * c2;
-      const float alpha = fast_exp2(m * c2 - ms);  // 0 while nothing was seen yet
-      m = m_new;
-      float psum = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(s[t][r], c2, -ms));
-          s[t][r] = e;
-          psum += e;
-        }
-      l = fmaf(l, alpha, psum);
-
-      if constexpr (DROPOUT) {
-        // One Philox call per 4 consecutive keys of this query row.
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const uint32_t key4 = (uint32_t)(kb + 32 * t + 8 * g + 4 * hh);
-            const u32x4 w = philox(key4 >> 2, (uint32_t)qi, (uint32_t)hi, (uint32_t)bi,
-                                   p.seed_lo, p.seed_hi);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              s[t][4 * g + e] = (w[e] >= p.drop_threshold) ? s[t][4 * g + e] * p.drop_scale : 0.0f;
-          }
-      }
-
-      // P^T in bf16: chunk cc covers keys 16cc .. 16cc+15 (k-slots match V^T below).
-      bf16x8 pb[4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[cc][e] = (bf16)s[cc >> 1][8 * (cc & 1) + e];
-
-#pragma unroll
-      for (int u = 0; u < D / 32; ++u)
+      for (int u = 0; u < DU; ++u)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
-
-      // O^T += V^T P^T.  The A operand needs V[key][dcol] for dcol = 32u + li and
-      // keys 16cc + 4hh + {0..3} (slots 0-3) and 16cc + 8 + 4hh + {0..3} (slots 4-7):
-      // two transposing reads of 4 x 16 blocks of the row-major V tile.
-      const int g16 = lane & 15;
-      const int trow = 4 * hh + (g16 >> 2);
-      const int tcol = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+    }
+  };
+  // The fused body of one pipeline step.  Phase A interleaves the MFMAs of
+  // the next score tile with the exponentials of the current one (two
+  // elements per MFMA for d = 128, four for d = 64); phase B interleaves the
+  // P V MFMAs with the next tile's row max.  The sched_group_barrier pattern
+  // pins that interleave and keeps the LDS operand reads one MFMA ahead
+  // instead of all hoisted to the top (which would exhaust the registers).
+  constexpr int NA = 2 * KC;          // phase-A MFMAs (next score tile)
+  constexpr int EPA = 32 / NA;        // exponentials per phase-A MFMA
+  auto body = [&](int jt, int kst, int vst, bool has_next, f32x16 (&s)[2], f32x16 (&sn)[2],
+                  bf16x8 (&pb)[4]) {
+    const float nm = mref == -INFINITY ? 0.0f : -mref;
+    const bf16* ks = kbuf(kst);
+    float ps = 0.0f;
 #pragma unroll
-      for (int u = 0; u < D / 32; ++u)
+    for (int i = 0; i < NA; ++i) {
+      const int t = i / KC, c = i % KC;
+      if (has_next) {
+        if (c == 0) {
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const bf16* vp = vs + (16 * cc + trow) * VP + 32 * u + tcol;
-          const bf16x4 lo = lds_read_tr4(vp);
-          const bf16x4 hi4 = lds_read_tr4(vp + 8 * VP);
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-          oacc[u] = mfma32(a, pb[cc], oacc[u]);
+          for (int r = 0; r < 16; ++r) sn[t][r] = 0.0f;
+        }
+        const bf16x8 a = *(const bf16x8*)(ks + koff[c] + t * 32 * D);
+        sn[t] = mfma32(a, qreg[c], sn[t]);
+      }
+#pragma unroll
+      for (int x = 0; x < EPA; ++x) {
+        const int k = i * EPA + x, tt = k >> 4, r = k & 15;
+        const float e = fast_exp2(fmaf(s[tt][r], c2, nm));
+        s[tt][r] = e;
+        ps += e;
+      }
+      if (has_next) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPA, 0);  // VALU
+      }
+    }
+    l += ps;
+    if constexpr (DROPOUT) {
+      // One Philox call per 4 consecutive keys of this query row.
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t key4 = (uint32_t)(jt * BN + 32 * t + 8 * g + 4 * hh);
+          const u32x4 w = philox(key4 >> 2, (uint32_t)qi, (uint32_t)hi, (uint32_t)bi, p.seed_lo,
+                                 p.seed_hi);
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            s[t][4 * g + x] = (w[x] >= p.drop_threshold) ? s[t][4 * g + x] * p.drop_scale : 0.0f;
         }
     }
-    if (jb + 1 < nkb) store_tile(cur ^ 1);
+    // chunk cc covers keys 16cc .. 16cc+15 (k-slots match V^T below)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) pb[cc][x] = (bf16)s[cc >> 1][8 * (cc & 1) + x];
+    // Phase B: O^T += V^T P^T.
+    const lds_bf16* vs = to_lds(vbuf(vst));
+#pragma unroll
+    for (int u = 0; u < DU; ++u)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const bf16x4 lo = lds_read_tr4(vs + voff[0][u] + 16 * cc * D);
+        const bf16x4 hi4 = lds_read_tr4(vs + voff[1][u] + 16 * cc * D);
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        oacc[u] = mfma32(a, pb[cc], oacc[u]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposing reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (row max of the next tile)
+      }
+  };
+
+  f32x16 scur[2];
+  float mx_cur = -INFINITY;
+  if (nkb > 0) {
+    issue_k(0, 0);
+    issue_v(0, 0);
+    if (nkb > 1) issue_k(1, 1);
+    wait_vmem();
     __syncthreads();
+    qk(0, scur);
+    if (nfree == 0) apply_mask(0, scur);
+    mx_cur = tile_max(scur);
   }
 
-  // Epilogue: O = O^T / l, LSE = scale*m + ln(l).
+  // One pipeline step for tile j (scores in scur, row max mx_cur):
+  //   rescale O if tile j moved the max; S_{j+1} = K_{j+1} Q^T; P_j = exp(S_j);
+  //   O += V_j^T P_j^T; row max of S_{j+1}.
+  // Loads of K_{j+2} and V_{j+1} are issued at the start and awaited at the end.
+  auto step = [&](int j, auto has_next_t, auto mask_next_t, auto par_t) {
+    constexpr bool HAS_NEXT = decltype(has_next_t)::value;
+    constexpr bool MASK_NEXT = decltype(mask_next_t)::value;
+    constexpr int PAR = decltype(par_t)::value;  // j & 1
+    __syncthreads();  // K_{j+1}, V_j resident; every wave is done with step j-1
+    if (j + 2 < nkb) issue_k(j + 2, PAR);
+    if (j + 1 < nkb) issue_v(j + 1, PAR ^ 1);
+    rescale_if_needed(mx_cur);
+    f32x16 snext[2];
+    bf16x8 pb[4];
+    body(j, PAR ^ 1, PAR, HAS_NEXT, scur, snext, pb);
+    if constexpr (HAS_NEXT) {
+      if constexpr (MASK_NEXT) apply_mask(j + 1, snext);
+      mx_cur = tile_max(snext);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) scur[t] = snext[t];
+    }
+    wait_vmem();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+
+  // The stage parity of every step is a compile-time constant: steps run in
+  // pairs from even indices.  Steps before jm (even, at most nfree - 1) have an
+  // unmasked next tile; later ones mask it (harmless where no key is masked).
+  int j = 0;
+  const int jm = max(nfree - 1, 0) & ~1;
+  for (; j < jm; j += 2) {
+    step(j, T{}, F{}, P0{});
+    step(j + 1, T{}, F{}, P1{});
+  }
+  for (; j + 2 < nkb; j += 2) {
+    step(j, T{}, T{}, P0{});
+    step(j + 1, T{}, T{}, P1{});
+  }
+  if (j + 1 < nkb) {
+    step(j, T{}, T{}, P0{});
+    ++j;
+  }
+  if (j < nkb) {  // the last tile: no next one
+    if (j & 1)
+      step(j, F{}, F{}, P1{});
+    else
+      step(j, F{}, F{}, P0{});
+  }
+
+  // Epilogue: O = O^T / l, LSE = (mref + log2 l) * ln 2.
   const float lt = pair_sum(l);
   if (qi < N) {
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     bf16* orow = p.o + head_off + (size_t)qi * D;
 #pragma unroll
-    for (int u = 0; u < D / 32; ++u)
+    for (int u = 0; u < DU; ++u)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         bf16x4 ov;
@@ -258,7 +382,7 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_bf16_kernel(FwdPara
         *(bf16x4*)(orow + 32 * u + 8 * g + 4 * hh) = ov;
       }
     if (hh == 0) {
-      p.lse[(size_t)head * N + qi] = lt > 0.0f ? (m * c2 + __log2f(lt)) * kLn2 : -INFINITY;
+      p.lse[(size_t)head * N + qi] = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
     }
   }
 }
