@@ -72,6 +72,17 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// An empty instruction that claims to read and rewrite x: the value must be
+// computed at this point of the program, which keeps a reduction step inside
+// the MFMA group it was written in instead of being sunk past the loop.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+// m = max(m, a, b) as one v_max3_f32, placed where it is written (the scores
+// are never NaN, so the operand canonicalisation fmaxf would add is not needed).
+__device__ __forceinline__ void max3_into(float& m, float a, float b) {
+  asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(a), "v"(b));
+}
+
 // Philox4x32-10 (Salmon et al., SC'11): ten rounds of
 //   (c0, c1, c2, c3) -> (hi(B*c2) ^ c1 ^ k0, lo(B*c2), hi(A*c0) ^ c3 ^ k1, lo(A*c0))
 // with A = 0xD2511F53, B = 0xCD9E8D57, the key advanced by the Weyl increments

@@ -100,7 +100,8 @@ void fwd_bf16_kernel(FwdParams p) {
   const int head = lid / p.num_qblocks;                            // b * H + h
   const int qb = p.num_qblocks - 1 - (lid - head * p.num_qblocks);  // costliest blocks first
   const int bi = head / p.H, hi = head - bi * p.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
   const int q0 = qb * C::BM;
   const int qw = q0 + wave * 32;  // first query of this wave
@@ -229,80 +230,7 @@ void fwd_bf16_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
     }
   };
-  // The fused body of one pipeline step.  Phase A interleaves the MFMAs of
-  // the next score tile with the exponentials of the current one (two
-  // elements per MFMA for d = 128, four for d = 64); phase B interleaves the
-  // P V MFMAs with the next tile's row max.  The sched_group_barrier pattern
-  // pins that interleave and keeps the LDS operand reads one MFMA ahead
-  // instead of all hoisted to the top (which would exhaust the registers).
-  constexpr int NA = 2 * KC;          // phase-A MFMAs (next score tile)
-  constexpr int EPA = 32 / NA;        // exponentials per phase-A MFMA
-  auto body = [&](int jt, int kst, int vst, bool has_next, f32x16 (&s)[2], f32x16 (&sn)[2],
-                  bf16x8 (&pb)[4]) {
-    const float nm = mref == -INFINITY ? 0.0f : -mref;
-    const bf16* ks = kbuf(kst);
-    float ps = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int t = i / KC, c = i % KC;
-      if (has_next) {
-        if (c == 0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sn[t][r] = 0.0f;
-        }
-        const bf16x8 a = *(const bf16x8*)(ks + koff[c] + t * 32 * D);
-        sn[t] = mfma32(a, qreg[c], sn[t]);
-      }
-#pragma unroll
-      for (int x = 0; x < EPA; ++x) {
-        const int k = i * EPA + x, tt = k >> 4, r = k & 15;
-        const float e = fast_exp2(fmaf(s[tt][r], c2, nm));
-        s[tt][r] = e;
-        ps += e;
-      }
-      if (has_next) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPA, 0);  // VALU
-      }
-    }
-    l += ps;
-    if constexpr (DROPOUT) {
-      // One Philox call per 4 consecutive keys of this query row.
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t key4 = (uint32_t)(jt * BN + 32 * t + 8 * g + 4 * hh);
-          const u32x4 w = philox(key4 >> 2, (uint32_t)qi, (uint32_t)hi, (uint32_t)bi, p.seed_lo,
-                                 p.seed_hi);
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            s[t][4 * g + x] = (w[x] >= p.drop_threshold) ? s[t][4 * g + x] * p.drop_scale : 0.0f;
-        }
-    }
-    // chunk cc covers keys 16cc .. 16cc+15 (k-slots match V^T below)
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-      for (int x = 0; x < 8; ++x) pb[cc][x] = (bf16)s[cc >> 1][8 * (cc & 1) + x];
-    // Phase B: O^T += V^T P^T.
-    const lds_bf16* vs = to_lds(vbuf(vst));
-#pragma unroll
-    for (int u = 0; u < DU; ++u)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const bf16x4 lo = lds_read_tr4(vs + voff[0][u] + 16 * cc * D);
-        const bf16x4 hi4 = lds_read_tr4(vs + voff[1][u] + 16 * cc * D);
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        oacc[u] = mfma32(a, pb[cc], oacc[u]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposing reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (row max of the next tile)
-      }
-  };
-
-  f32x16 scur[2];
+  f32x16 sa[2], sb[2];  // score tiles of the current and the next step, alternating
   float mx_cur = -INFINITY;
   if (nkb > 0) {
     issue_k(0, 0);
@@ -310,16 +238,27 @@ void fwd_bf16_kernel(FwdParams p) {
     if (nkb > 1) issue_k(1, 1);
     wait_vmem();
     __syncthreads();
-    qk(0, scur);
-    if (nfree == 0) apply_mask(0, scur);
-    mx_cur = tile_max(scur);
+    qk(0, sa);
+    if (nfree == 0) apply_mask(0, sa);
+    mx_cur = tile_max(sa);
   }
 
-  // One pipeline step for tile j (scores in scur, row max mx_cur):
-  //   rescale O if tile j moved the max; S_{j+1} = K_{j+1} Q^T; P_j = exp(S_j);
-  //   O += V_j^T P_j^T; row max of S_{j+1}.
-  // Loads of K_{j+2} and V_{j+1} are issued at the start and awaited at the end.
-  auto step = [&](int j, auto has_next_t, auto mask_next_t, auto par_t) {
+  // One pipeline step for tile j (scores in scur, row max mx_cur).
+  //   Phase A: the MFMAs of S_{j+1} = K_{j+1} Q^T, each followed by the
+  //            exponentials (and bf16 packing) of EPA elements of S_j.
+  //   Phase B: the MFMAs of O^T += V_j^T P_j^T, each followed by a share of
+  //            the mask and row max of S_{j+1}.
+  // LDS operand reads run one MFMA ahead through a two-entry register ring;
+  // a scheduling fence after every MFMA group pins that order (left alone,
+  // the scheduler either hoists all reads, exhausting the registers, or
+  // issues each read right before its MFMA and waits for it).  Loads of K_{j+2} and
+  // V_{j+1} are issued at the start and awaited at the end of the step.
+  constexpr int NA = 2 * KC;    // phase-A MFMAs
+  constexpr int EPA = 32 / NA;  // exponentials per phase-A MFMA
+  constexpr int NB = 4 * DU;    // phase-B MFMAs
+  constexpr int MPB = 32 / NB;  // row-max elements per phase-B MFMA
+  auto step = [&](int j, auto has_next_t, auto mask_next_t, auto par_t, f32x16 (&scur)[2],
+                  f32x16 (&sn)[2]) {
     constexpr bool HAS_NEXT = decltype(has_next_t)::value;
     constexpr bool MASK_NEXT = decltype(mask_next_t)::value;
     constexpr int PAR = decltype(par_t)::value;  // j & 1
@@ -327,15 +266,91 @@ void fwd_bf16_kernel(FwdParams p) {
     if (j + 2 < nkb) issue_k(j + 2, PAR);
     if (j + 1 < nkb) issue_v(j + 1, PAR ^ 1);
     rescale_if_needed(mx_cur);
-    f32x16 snext[2];
+    const float nm = mref == -INFINITY ? 0.0f : -mref;
+
+    // ---- phase A
+    const bf16* ks = kbuf(PAR ^ 1);
+    auto kread = [&](int i) { return *(const bf16x8*)(ks + koff[i % KC] + (i / KC) * 32 * D); };
     bf16x8 pb[4];
-    body(j, PAR ^ 1, PAR, HAS_NEXT, scur, snext, pb);
-    if constexpr (HAS_NEXT) {
-      if constexpr (MASK_NEXT) apply_mask(j + 1, snext);
-      mx_cur = tile_max(snext);
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 ka[2];
+    if constexpr (HAS_NEXT) ka[0] = kread(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) scur[t] = snext[t];
+    for (int i = 0; i < NA; ++i) {
+      const int t = i / KC, c = i % KC;
+      if constexpr (HAS_NEXT) {
+        if (i + 1 < NA) ka[(i + 1) & 1] = kread(i + 1);
+        const f32x16 zero = {};
+        sn[t] = mfma32(ka[i & 1], qreg[c], c == 0 ? zero : sn[t]);
+      }
+#pragma unroll
+      for (int x = 0; x < EPA; ++x) {
+        const int k = i * EPA + x, tt = k >> 4, r = k & 15;
+        const float e = fast_exp2(fmaf(scur[tt][r], c2, nm));
+        scur[tt][r] = e;
+        ps[k & 3] += e;
+        pin(ps[k & 3]);  // keep the sum here, between this group's MFMAs
+      }
+      if constexpr (!DROPOUT) {
+        // pack the finished pairs: element k lives in pb[k >> 3][k & 7]
+#pragma unroll
+        for (int x = 0; x < EPA; x += 2) {
+          const int k = i * EPA + x, tt = k >> 4, r = k & 15;
+          pb[k >> 3][k & 7] = (bf16)scur[tt][r];
+          pb[k >> 3][(k & 7) + 1] = (bf16)scur[tt][r + 1];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // nothing crosses: keeps the ring one MFMA ahead
     }
+    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    if constexpr (DROPOUT) {
+      // One Philox call per 4 consecutive keys of this query row.
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t key4 = (uint32_t)(j * BN + 32 * t + 8 * g + 4 * hh);
+          const u32x4 w = philox(key4 >> 2, (uint32_t)qi, (uint32_t)hi, (uint32_t)bi, p.seed_lo,
+                                 p.seed_hi);
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            scur[t][4 * g + x] =
+                (w[x] >= p.drop_threshold) ? scur[t][4 * g + x] * p.drop_scale : 0.0f;
+        }
+#pragma unroll
+      for (int k = 0; k < 32; ++k) pb[k >> 3][k & 7] = (bf16)scur[k >> 4][k & 15];
+    }
+    // chunk cc of pb covers keys 16cc .. 16cc+15; its k-slots match V^T below.
+
+    // ---- phase B
+    if constexpr (HAS_NEXT && MASK_NEXT) apply_mask(j + 1, sn);
+    const lds_bf16* vs = to_lds(vbuf(PAR));
+    auto vread = [&](int idx) {
+      const int u = idx / 4, cc = idx % 4;
+      const bf16x4 lo = lds_read_tr4(vs + voff[0][u] + 16 * cc * D);
+      const bf16x4 hi4 = lds_read_tr4(vs + voff[1][u] + 16 * cc * D);
+      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      return a;
+    };
+    float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    bf16x8 va[2];
+    va[0] = vread(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int idx = 0; idx < NB; ++idx) {
+      if (idx + 1 < NB) va[(idx + 1) & 1] = vread(idx + 1);
+      oacc[idx / 4] = mfma32(va[idx & 1], pb[idx % 4], oacc[idx / 4]);
+      if constexpr (HAS_NEXT) {
+#pragma unroll
+        for (int x = 0; x < MPB; x += 2) {
+          const int k = idx * MPB + x, q = (k >> 1) & 3;
+          max3_into(mp[q], sn[k >> 4][k & 15], sn[k >> 4][(k & 15) + 1]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (HAS_NEXT) mx_cur = pair_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]))) * c2;
     wait_vmem();
   };
   using T = std::true_type;
@@ -349,22 +364,24 @@ void fwd_bf16_kernel(FwdParams p) {
   int j = 0;
   const int jm = max(nfree - 1, 0) & ~1;
   for (; j < jm; j += 2) {
-    step(j, T{}, F{}, P0{});
-    step(j + 1, T{}, F{}, P1{});
+    step(j, T{}, F{}, P0{}, sa, sb);
+    step(j + 1, T{}, F{}, P1{}, sb, sa);
   }
   for (; j + 2 < nkb; j += 2) {
-    step(j, T{}, T{}, P0{});
-    step(j + 1, T{}, T{}, P1{});
+    step(j, T{}, T{}, P0{}, sa, sb);
+    step(j + 1, T{}, T{}, P1{}, sb, sa);
   }
   if (j + 1 < nkb) {
-    step(j, T{}, T{}, P0{});
+    step(j, T{}, T{}, P0{}, sa, sb);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sa[t] = sb[t];
     ++j;
   }
   if (j < nkb) {  // the last tile: no next one
     if (j & 1)
-      step(j, F{}, F{}, P1{});
+      step(j, F{}, F{}, P1{}, sa, sb);
     else
-      step(j, F{}, F{}, P0{});
+      step(j, F{}, F{}, P0{}, sa, sb);
   }
 
   // Epilogue: O = O^T / l, LSE = (mref + log2 l) * ln 2.
