@@ -3,7 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_internal.hpp"
 
 namespace {

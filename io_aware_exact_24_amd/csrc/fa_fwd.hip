@@ -248,7 +248,7 @@ void fwd_bf16_kernel(FwdParams p) {
   //            exponentials (and bf16 packing) of EPA elements of S_j.
   //   Phase B: the MFMAs of O^T += V_j^T P_j^T, each followed by a share of
   //            the mask and row max of S_{j+1}.
-  // LDS operand reads run one MFMA ahead through a two-entry register ring;
+  // LDS operand reads run two MFMAs ahead through a three-entry register ring;
   // a scheduling fence after every MFMA group pins that order (left alone,
   // the scheduler either hoists all reads, exhausting the registers, or
   // issues each read right before its MFMA and waits for it).  Loads of K_{j+2} and
@@ -273,16 +273,19 @@ void fwd_bf16_kernel(FwdParams p) {
     auto kread = [&](int i) { return *(const bf16x8*)(ks + koff[i % KC] + (i / KC) * 32 * D); };
     bf16x8 pb[4];
     float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    bf16x8 ka[2];
-    if constexpr (HAS_NEXT) ka[0] = kread(0);
+    bf16x8 ka[3];
+    if constexpr (HAS_NEXT) {
+      ka[0] = kread(0);
+      ka[1] = kread(1);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int t = i / KC, c = i % KC;
       if constexpr (HAS_NEXT) {
-        if (i + 1 < NA) ka[(i + 1) & 1] = kread(i + 1);
+        if (i + 2 < NA) ka[(i + 2) % 3] = kread(i + 2);
         const f32x16 zero = {};
-        sn[t] = mfma32(ka[i & 1], qreg[c], c == 0 ? zero : sn[t]);
+        sn[t] = mfma32(ka[i % 3], qreg[c], c == 0 ? zero : sn[t]);
       }
 #pragma unroll
       for (int x = 0; x < EPA; ++x) {
@@ -334,13 +337,14 @@ void fwd_bf16_kernel(FwdParams p) {
       return a;
     };
     float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    bf16x8 va[2];
+    bf16x8 va[3];
     va[0] = vread(0);
+    va[1] = vread(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int idx = 0; idx < NB; ++idx) {
-      if (idx + 1 < NB) va[(idx + 1) & 1] = vread(idx + 1);
-      oacc[idx / 4] = mfma32(va[idx & 1], pb[idx % 4], oacc[idx / 4]);
+      if (idx + 2 < NB) va[(idx + 2) % 3] = vread(idx + 2);
+      oacc[idx / 4] = mfma32(va[idx % 3], pb[idx % 4], oacc[idx / 4]);
       if constexpr (HAS_NEXT) {
 #pragma unroll
         for (int x = 0; x < MPB; x += 2) {
