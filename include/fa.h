@@ -104,7 +104,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: an fp32 [B, H, N, d]
- * dQ accumulator followed by the fp32 [B, H, N] row terms D_i = sum_k dO_ik O_ik.
+ * dQ accumulator followed by two fp32 [B, H, N] row arrays, D_i =
+ * sum_k dO_ik O_ik and LSE_i * log2(e), each padded to a multiple of 256 bytes.
  * Returns 0 for arguments fa_bwd would reject.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype);

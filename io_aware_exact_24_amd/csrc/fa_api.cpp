@@ -83,10 +83,11 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype) {
   const int64_t n = elems(B, H, N, d);
   if (n < 0) return 0;
   const int64_t rows = (int64_t)B * H * N;
-  // fp32 dQ accumulator, then fp32 D, each rounded up to 256 bytes.
+  // fp32 dQ accumulator, then fp32 D and fp32 LSE*log2(e), each rounded up to
+  // 256 bytes.
   const size_t acc = ((size_t)n * 4 + 255) & ~(size_t)255;
   const size_t dl = ((size_t)rows * 4 + 255) & ~(size_t)255;
-  return acc + dl;
+  return acc + 2 * dl;
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -130,6 +131,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.seed = seed;
   a.dq_acc = (float*)workspace;
   a.delta = (float*)((char*)workspace + (((size_t)n * 4 + 255) & ~(size_t)255));
+  a.lse2 = (float*)((char*)a.delta + ((((size_t)B * H * N) * 4 + 255) & ~(size_t)255));
   const hipError_t e = fa::launch_bwd_bf16(a, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

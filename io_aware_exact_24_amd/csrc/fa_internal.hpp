@@ -42,7 +42,8 @@ struct BwdArgs {
   float drop_scale;
   uint64_t seed;
   float* dq_acc;  // workspace: fp32 [B, H, N, d]
-  float* delta;   // workspace: fp32 [B, H, N]
+  float* delta;   // workspace: fp32 [B, H, N], D_i = sum_k dO_ik O_ik
+  float* lse2;    // workspace: fp32 [B, H, N], LSE_i * log2(e)
 };
 
 // Each returns hipSuccess or the launch error.
