@@ -103,9 +103,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes: an fp32 [B, H, N, d]
- * dQ accumulator followed by two fp32 [B, H, N] row arrays, D_i =
- * sum_k dO_ik O_ik and LSE_i * log2(e), each padded to a multiple of 256 bytes.
+ * Bytes of device workspace fa_bwd needs for these sizes: two fp32 [B, H, N]
+ * row arrays, D_i = sum_k dO_ik O_ik and LSE_i * log2(e), each padded to a
+ * multiple of 256 bytes.
  * Returns 0 for arguments fa_bwd would reject.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype);
@@ -122,8 +122,9 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype);
  *                     16-byte aligned; its contents on entry do not matter and
  *                     are garbage on exit.
  *
- * dtype FA_BF16 only (d in {64, 128}).  dK and dV are bitwise deterministic;
- * dQ is accumulated with fp32 atomics, so its last bits may vary between runs.
+ * dtype FA_BF16 only (d in {64, 128}).  dQ, dK and dV are bitwise
+ * deterministic: each is accumulated in fp32 registers by one workgroup and
+ * written once (no atomics).
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse, void* dq, void* dk, void* dv,

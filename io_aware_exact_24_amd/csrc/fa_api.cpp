@@ -30,6 +30,11 @@ uint32_t drop_threshold(float p) {
 
 float drop_scale(float p) { return (float)(1.0 / (1.0 - (double)p)); }
 
+// One fp32 value per row (B * H * N of them), rounded up to 256 bytes.
+size_t row_array_bytes(int B, int H, int N) {
+  return (((size_t)B * H * N) * 4 + 255) & ~(size_t)255;
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,14 +85,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype) {
   if (dtype != FA_BF16 || (d != 64 && d != 128)) return 0;
-  const int64_t n = elems(B, H, N, d);
-  if (n < 0) return 0;
-  const int64_t rows = (int64_t)B * H * N;
-  // fp32 dQ accumulator, then fp32 D and fp32 LSE*log2(e), each rounded up to
-  // 256 bytes.
-  const size_t acc = ((size_t)n * 4 + 255) & ~(size_t)255;
-  const size_t dl = ((size_t)rows * 4 + 255) & ~(size_t)255;
-  return acc + 2 * dl;
+  if (elems(B, H, N, d) < 0) return 0;
+  return 2 * row_array_bytes(B, H, N);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -129,9 +128,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.drop_threshold = drop_threshold(dropout_p);
   a.drop_scale = drop_scale(dropout_p);
   a.seed = seed;
-  a.dq_acc = (float*)workspace;
-  a.delta = (float*)((char*)workspace + (((size_t)n * 4 + 255) & ~(size_t)255));
-  a.lse2 = (float*)((char*)a.delta + ((((size_t)B * H * N) * 4 + 255) & ~(size_t)255));
+  // workspace: D, then LSE * log2(e)
+  a.delta = (float*)workspace;
+  a.lse2 = (float*)((char*)workspace + row_array_bytes(B, H, N));
   const hipError_t e = fa::launch_bwd_bf16(a, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

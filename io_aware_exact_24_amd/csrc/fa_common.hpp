@@ -107,6 +107,22 @@ __device__ __forceinline__ u32x4 philox(uint32_t c0, uint32_t c1, uint32_t c2, u
   return out;
 }
 
+// XOR swizzle of the 16-byte chunks of a row-major bf16 tile with D-element
+// rows: the physical chunk slot of logical chunk c in tile row r is c ^ swz(r).
+// d = 128 (16 chunks, 256-byte rows): 16 consecutive rows get 16 distinct
+// values (row reads of 16 lanes hit all 64 banks once) and 4 aligned
+// consecutive rows differ in bits 2-3 (the transposing read of 4 rows x 64
+// bytes hits 4 different 64-byte bank groups).  d = 64 (8 chunks, 128-byte
+// rows): the same two properties with two rows per 256-byte bank cycle.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+}
+
 // Remap a linear workgroup id so that consecutive logical ids run on the same
 // XCD.  The dispatcher deals workgroups round-robin to the 8 XCDs, so physical
 // id p lands on XCD p % 8; logical id (p % 8) * (G / 8) + p / 8 puts each XCD's
@@ -138,5 +154,14 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, const void* 
 // Wait until this wave's outstanding vector-memory loads (including LDS DMA)
 // have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N of this wave's vector-memory operations are still
+// outstanding.  They complete in issue order, so operations issued before the
+// last N are done (N <= 63; the count is split over bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 }  // namespace fa

@@ -63,21 +63,6 @@ struct FwdCfg {
   static_assert(LOADS * THREADS == BN * CHUNKS, "tile/thread mismatch");
 };
 
-// Physical 16-byte chunk slot of logical chunk c in tile row r is c ^ swz(r).
-// d = 128 (16 chunks, 256-byte rows): 16 consecutive rows get 16 distinct
-// values (row reads of 16 lanes hit all 64 banks once) and 4 aligned
-// consecutive rows differ in bits 2-3 (the transposing read of 4 rows x 64
-// bytes hits 4 different 64-byte bank groups).  d = 64 (8 chunks, 128-byte
-// rows): the same two properties with two rows per 256-byte bank cycle.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) {
-    return ((r & 3) << 2) | ((r >> 2) & 3);
-  } else {
-    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  }
-}
-
 template <int D, bool CAUSAL, bool DROPOUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdParams p) {

@@ -41,7 +41,6 @@ struct BwdArgs {
   uint32_t drop_threshold;
   float drop_scale;
   uint64_t seed;
-  float* dq_acc;  // workspace: fp32 [B, H, N, d]
   float* delta;   // workspace: fp32 [B, H, N], D_i = sum_k dO_ik O_ik
   float* lse2;    // workspace: fp32 [B, H, N], LSE_i * log2(e)
 };
