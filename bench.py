@@ -4,20 +4,25 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 One step is the whole hot path on the causal decoder workload (B=4, H=32,
-N=4096, d=128, bf16, i.i.d. N(0,1) inputs drawn from a fixed seed): one fa_fwd
-(O and LSE) followed by one fa_bwd (D preprocess, recompute backward, dQ
-convert), inputs resident in device memory.  W untimed steps, then exactly K
-timed steps between device synchronisations.  Prints one JSON line.
+N=4096, d=128, bf16, i.i.d. N(0,1) inputs drawn from a fixed seed): fa_fwd (O
+and LSE), then the backward as its three stages (fa_bwd_preprocess,
+fa_bwd_dkdv, fa_bwd_dq, exactly what fa_bwd enqueues) on the same stream,
+inputs resident in device memory.  W untimed steps, then exactly K timed steps
+between device synchronisations; HIP events between the launches give each
+kernel's duration.  Prints one JSON line.
 
-FLOP convention (causal halves the work): forward 4*B*H*N^2*d/2, backward 2.5x
-the forward (five N x N x d products including the recomputed Q K^T).
-Roofline peak: MI355X dense bf16 MFMA, 2500 TFLOP/s (published).
+FLOP convention (algorithmic, causal halves the work): forward 4*B*H*N^2*d/2
+(two N x N x d products), backward 2.5x the forward (five products including
+the recomputed Q K^T).  Per kernel: the dK/dV kernel performs four of the
+products (S, dP, dV, dK) and the dQ kernel three (S, dP, dQ); the rooflines use
+those counts.  Peak: MI355X dense bf16 MFMA, 2500 TFLOP/s (published).
 """
 
 import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -26,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
 WORKLOAD_NUMBER = 3
+CPU_SAMPLE_HEADS = 8  # heads of the workload the oracle processes for the CPU baseline
 
 
 def flops(B, H, N, d, causal):
@@ -43,32 +49,33 @@ def source_digest():
 
 
 def stored_traffic(kernel):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    when the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/traffic_decoder_causal.md, or None when the kernel sources changed
+    since the counters were taken (the summary records a digest of csrc/)."""
+    path = os.path.join(ROOT, "profiles", "traffic_decoder_causal.md")
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        rec = json.load(f)
-    if rec.get("source_digest") != source_digest():
+    text = open(path).read()
+    m = re.search(r"source digest: `([0-9a-f]+)`", text)
+    if not m or m.group(1) != source_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    m = re.search(r"^\| `" + re.escape(kernel) + r"` \|[^|]*\|[^|]*\| ([0-9.e+]+) \|", text, re.M)
+    return float(m.group(1)) if m else None
 
 
-def cpu_baseline(w, budget_s=30.0):
-    """The oracle, untouched, on one head of the workload (fwd + bwd), timed on
-    the host cores; scaled to the metric's unit (algorithmic TFLOP/s)."""
-    import numpy as np
-
+def cpu_baseline(w, heads=CPU_SAMPLE_HEADS):
+    """The oracle, untouched, on `heads` heads of the workload (forward +
+    backward, one head at a time as it is written), timed on the host cores;
+    scaled to the metric's unit (algorithmic TFLOP/s)."""
     from io_aware_exact_24_amd.workloads import draw
     from oracle import attention_backward, attention_forward
 
-    inp = draw(1, 1, w.N, w.d, w.torch_dtype, seed=w.seed)
+    inp = draw(1, heads, w.N, w.d, w.torch_dtype, seed=w.seed)
     t0 = time.perf_counter()
     attention_forward(inp.q, inp.k, inp.v, w.scale, w.causal)
     attention_backward(inp.q, inp.k, inp.v, inp.dout, w.scale, w.causal)
     dt = time.perf_counter() - t0
-    ff, fb = flops(1, 1, w.N, w.d, w.causal)
+    ff, fb = flops(1, heads, w.N, w.d, w.causal)
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -79,14 +86,78 @@ def cpu_baseline(w, budget_s=30.0):
         "unit": "TFLOP/s",
         "cores": min(cores, threads),
         "kind": "oracle",
-        "sample": f"one head (B=1, H=1) of the workload, forward + backward, fp64 numpy, "
-                  f"{dt:.1f} s wall",
-        "seconds": dt,
-        "numpy_blas_threads_hint": threads,
+        "sample": f"{heads} heads (B=1, H={heads}, N={w.N}, d={w.d}, causal) of the workload, "
+                  f"forward + backward, fp64 numpy, {dt:.1f} s wall",
+        "seconds": round(dt, 2),
     }
 
 
+def summarize_traffic(fetch_dir, write_dir, out_path):
+    """Turn two rocprofv3 --pmc runs of `bench.py --calibrate-copy` (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch) into HBM bytes per launch of each
+    kernel.  Each counter is scaled by what it reads for the plain 256 MiB
+    device copy the run starts with (true bytes: 256 MiB read, 256 MiB
+    written), and the result is written as a markdown table tagged with the
+    digest of the kernel sources it was measured on."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def load(d, counter):
+        vals = defaultdict(list)
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if not copy:
+        raise SystemExit("no copy kernel in the counter runs (run bench.py --calibrate-copy)")
+    true_kib = 256 * 1024.0
+    f_scale = true_kib / (sum(fetch[copy[0]]) / len(fetch[copy[0]]))
+    w_scale = true_kib / (sum(write[copy[0]]) / len(write[copy[0]]))
+    rows = []
+    for k in sorted(fetch):
+        m = re.search(r"(\w+_kernel)", k)
+        if not m or "fa::" not in k or k not in write:
+            continue
+        fk = sum(fetch[k]) / len(fetch[k]) * f_scale * 1024
+        wk = sum(write[k]) / len(write[k]) * w_scale * 1024
+        rows.append((m.group(1), fk, wk))
+    lines = [
+        "# HBM traffic per launch: decoder_causal workload (B=4, H=32, N=4096, d=128, causal, bf16)",
+        "",
+        "Commands (from the repository root, one MI355X):",
+        "",
+        "```",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch -o p -- "
+        "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write -o p -- "
+        "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
+        "python bench.py --summarize-traffic gpurun_out/pmc/fetch gpurun_out/pmc/write",
+        "```",
+        "",
+        f"Calibration on the plain 256 MiB copy: FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f} "
+        "give true bytes.",
+        "",
+        f"source digest: `{source_digest()}`",
+        "",
+        "| kernel | read (MiB) | written (MiB) | total bytes per launch |",
+        "|---|---|---|---|",
+    ]
+    for name, fk, wk in rows:
+        lines.append(f"| `{name}` | {fk / 2**20:.1f} | {wk / 2**20:.1f} | {fk + wk:.4e} |")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
+    if len(sys.argv) == 4 and sys.argv[1] == "--summarize-traffic":
+        summarize_traffic(sys.argv[2], sys.argv[3],
+                          os.path.join(ROOT, "profiles", "traffic_decoder_causal.md"))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -96,8 +167,9 @@ def main():
                     help="first run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("this benchmark runs on exactly one GPU (the attention path has no multi-GPU "
-              "component here); use --gpus 1", file=sys.stderr)
+        print("this benchmark runs on exactly one GPU: the attention path here has no multi-GPU "
+              "component (heads and batch entries shard with no exchange); use --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -126,21 +198,29 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+
     def step(ev=None):
+        launches = (
+            lambda: binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, 0.0, 0, stream),
+            lambda: binding.fa_bwd_preprocess(o, do, lse, ws, stream),
+            lambda: binding.fa_bwd_dkdv(q, k, v, do, dk, dv, w.scale, w.causal, None, 0.0, 0, ws,
+                                        stream),
+            lambda: binding.fa_bwd_dq(q, k, v, do, dq, w.scale, w.causal, None, 0.0, 0, ws, stream),
+        )
+        for i, launch in enumerate(launches):
+            if ev is not None:
+                ev[i].record(stream)
+            launch()
         if ev is not None:
-            ev[0].record(stream)
-        binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, 0.0, 0, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        binding.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.scale, w.causal, None, 0.0, 0, ws, stream)
-        if ev is not None:
-            ev[2].record(stream)
+            ev[len(launches)].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -148,32 +228,31 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
-    bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in events)
-    avg_fwd = sum(fwd_ms) / len(fwd_ms)
-    avg_bwd = sum(bwd_ms) / len(bwd_ms)
+    per = {n: sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps
+           for i, n in enumerate(names)}
+    avg_fwd = per["fwd"]
+    avg_bwd = per["bwd_pre"] + per["bwd_dkdv"] + per["bwd_dq"]
     ms_per_step = wall * 1e3 / args.steps
     ff, fb = flops(B, H, N, d, w.causal)
-    fwd_tf = ff / (avg_fwd * 1e-3) / 1e12
-    bwd_tf = fb / (avg_bwd * 1e-3) / 1e12
     value = (ff + fb) / (ms_per_step * 1e-3) / 1e12
 
-    # Dominant kernel: the backward (2.5x the forward's work).  Its launch time
-    # is the whole fa_bwd call (D preprocess + main + dQ convert) between HIP
-    # events on the library's stream, so the achieved rate is a lower bound for
-    # the main kernel alone.
-    dom, dom_ms, dom_flops = ("bwd_main", avg_bwd, fb) if avg_bwd >= avg_fwd else ("fwd", avg_fwd, ff)
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    # Algorithmic FLOP per launch of each compute kernel: the forward does two
+    # N x N x d products per (query, key) pair, the dK/dV kernel four, the dQ
+    # kernel three (fb is five).
+    kflops = {"fwd": ff, "bwd_dkdv": fb * 4 / 5, "bwd_dq": fb * 3 / 5}
+    kernel_names = {"fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
+    dom = max(kflops, key=lambda n: per[n])
+    achieved = kflops[dom] / (per[dom] * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
-        "kernel": dom,
+        "kernel": kernel_names[dom],
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": stored_traffic(dom),
-        "launch_ms": round(dom_ms, 4),
-        "flop_per_launch": dom_flops,
+        "traffic": stored_traffic(kernel_names[dom]),
+        "launch_ms": round(per[dom], 4),
+        "flop_per_launch": kflops[dom],
     }
     rec = {
         "metric": "attention fwd/bwd TFLOP/s at N=4096,d=128 causal bf16; % of MFMA peak",
@@ -190,10 +269,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decoder_causal: B=4 H=32 N=4096 d=128 causal bf16, N(0,1) inputs",
                    "B": B, "H": H, "N": N, "d": d, "causal": True, "dropout_p": 0.0},
-        "fwd": {"ms": round(avg_fwd, 4), "tflops": round(fwd_tf, 2),
-                "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
-        "bwd": {"ms": round(avg_bwd, 4), "tflops": round(bwd_tf, 2),
-                "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "fwd": {"ms": round(avg_fwd, 4), "tflops": round(ff / (avg_fwd * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(ff / (avg_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(avg_bwd, 4), "tflops": round(fb / (avg_bwd * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(fb / (avg_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "kernels_ms": {n: round(per[n], 4) for n in names},
         "roofline": roofline,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w),
     }

@@ -132,6 +132,37 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const int32_t* key_lens, float dropout_p, uint64_t seed,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * The three stages fa_bwd runs, in order, on its stream.  They are exported
+ * so that a caller can time them or overlap the two independent ones: once
+ * fa_bwd_preprocess has completed, fa_bwd_dkdv and fa_bwd_dq only read the
+ * inputs and the workspace and write disjoint outputs, so they may run on two
+ * streams at once.  Arguments have the meaning and checks of fa_bwd; the
+ * workspace must be the one fa_bwd_preprocess filled for the same o, dout
+ * and lse, and must not change while the other stages run.
+ *
+ * fa_bwd_preprocess: D_i = sum_k dO_ik O_ik and LSE_i * log2(e) into the
+ *   workspace (the backward's per-row terms).
+ * fa_bwd_dkdv: dK and dV.  Each 128-key block is one workgroup that walks the
+ *   query tiles, recomputing S = scale Q K^T and dP = dO V^T from Q, K, V and
+ *   the saved normaliser (ML Canon 48 FlashAttention, "backward without N x
+ *   N"; Flash Attention hardware-aware optimisation, section 2.2).
+ * fa_bwd_dq: dQ.  Each 128-query block is one workgroup that walks the key
+ *   tiles, recomputing S and dP the same way.
+ */
+fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
+                            int B, int H, int N, int d, fa_dtype dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                      void* dk, void* dv, int B, int H, int N, int d, fa_dtype dtype,
+                      float scale, int causal, const int32_t* key_lens, float dropout_p,
+                      uint64_t seed, const void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                    int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                    const int32_t* key_lens, float dropout_p, uint64_t seed,
+                    const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* fa_status_string(fa_status s);
 

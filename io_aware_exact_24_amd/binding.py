@@ -16,7 +16,8 @@ LIB_NAME = "libfa.so"
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F32, FA_BF16 = 0, 1
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_bwd_preprocess",
+           "fa_bwd_dkdv", "fa_bwd_dq")
 
 _lib = None
 
@@ -50,6 +51,12 @@ def load_library():
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [i]
+    lib.fa_bwd_preprocess.restype = i
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_dkdv.restype = i
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64, vp, sz, vp]
+    lib.fa_bwd_dq.restype = i
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -140,6 +147,56 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None
                     _stream(stream, q.device))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def _bwd_common(q, tensors, lse, key_lens, workspace):
+    import torch
+
+    B, H, N, d = q.shape
+    for name, t in tensors:
+        _check(t, q.shape, q.dtype, q.device, name)
+    if lse is not None:
+        _check(lse, (B, H, N), torch.float32, q.device, "lse")
+    kl = _key_lens(key_lens, B, q.device)
+    if workspace is None:
+        raise ValueError("the backward stages need a workspace tensor (see fa_bwd_workspace_size)")
+    return B, H, N, d, kl, workspace.numel() * workspace.element_size()
+
+
+def fa_bwd_preprocess(o, dout, lse, workspace, stream=None):
+    """Enqueue the backward preprocessing (per-row D and LSE*log2e into the workspace)."""
+    B, H, N, d, _, ws_bytes = _bwd_common(o, (("dout", dout),), lse, None, workspace)
+    st = load_library().fa_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(lse), B, H, N, d,
+                                          _dtype_code(o), _ptr(workspace), ws_bytes,
+                                          _stream(stream, o.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_preprocess")
+
+
+def fa_bwd_dkdv(q, k, v, dout, dk, dv, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
+                workspace=None, stream=None):
+    """Enqueue the dK/dV stage (after fa_bwd_preprocess filled the workspace)."""
+    B, H, N, d, kl, ws_bytes = _bwd_common(
+        q, (("k", k), ("v", v), ("dout", dout), ("dk", dk), ("dv", dv)), None, key_lens, workspace)
+    st = load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dk), _ptr(dv), B, H,
+                                    N, d, _dtype_code(q), float(scale), int(bool(causal)), _ptr(kl),
+                                    float(dropout_p), int(seed), _ptr(workspace), ws_bytes,
+                                    _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dkdv")
+
+
+def fa_bwd_dq(q, k, v, dout, dq, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
+              workspace=None, stream=None):
+    """Enqueue the dQ stage (after fa_bwd_preprocess filled the workspace)."""
+    B, H, N, d, kl, ws_bytes = _bwd_common(
+        q, (("k", k), ("v", v), ("dout", dout), ("dq", dq)), None, key_lens, workspace)
+    st = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), B, H, N, d,
+                                  _dtype_code(q), float(scale), int(bool(causal)), _ptr(kl),
+                                  float(dropout_p), int(seed), _ptr(workspace), ws_bytes,
+                                  _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dq")
 
 
 def forward(q, k, v, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0, stream=None):

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "fa.h"
 #include "fa_internal.hpp"
 
@@ -89,24 +91,33 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype) {
   return 2 * row_array_bytes(B, H, N);
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                 fa_dtype dtype, float scale, int causal, const int32_t* key_lens, float dropout_p,
-                 uint64_t seed, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
-      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
-    return FA_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by fa_bwd and its stages; pointers that a stage does not use
+// are passed as a non-null aligned placeholder by that stage.
+fa_status check_bwd(std::initializer_list<const void*> ptrs, const int32_t* key_lens, int B, int H,
+                    int N, int d, fa_dtype dtype, float scale, float dropout_p,
+                    const void* workspace, size_t workspace_bytes) {
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
   if (key_lens != nullptr && ((uintptr_t)key_lens & 3u) != 0) return FA_ERR_INVALID_ARG;
-  const int64_t n = elems(B, H, N, d);
-  if (n < 0) return FA_ERR_INVALID_ARG;
+  if (elems(B, H, N, d) < 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale <= 0.0f) return FA_ERR_INVALID_ARG;
   if (!valid_dropout(dropout_p)) return FA_ERR_INVALID_ARG;
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-  const size_t need = fa_bwd_workspace_size(B, H, N, d, dtype);
-  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d, dtype)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
 
+fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                  float scale, int causal, const int32_t* key_lens, float dropout_p, uint64_t seed,
+                  void* workspace, int stages, hipStream_t stream) {
   fa::BwdArgs a;
   a.q = q;
   a.k = k;
@@ -131,8 +142,57 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   // workspace: D, then LSE * log2(e)
   a.delta = (float*)workspace;
   a.lse2 = (float*)((char*)workspace + row_array_bytes(B, H, N));
-  const hipError_t e = fa::launch_bwd_bf16(a, stream);
+  const hipError_t e = fa::launch_bwd_bf16(a, stages, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const void* const kUnused = (const void*)(uintptr_t)16;  // aligned, never dereferenced
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                 fa_dtype dtype, float scale, int causal, const int32_t* key_lens, float dropout_p,
+                 uint64_t seed, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const fa_status st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, key_lens, B, H, N, d, dtype,
+                                 scale, dropout_p, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens, dropout_p,
+                 seed, workspace, fa::kBwdAll, stream);
+}
+
+fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N,
+                            int d, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  const fa_status st = check_bwd({o, dout, lse}, nullptr, B, H, N, d, dtype, 1.0f, 0.0f, workspace,
+                                 workspace_bytes);
+  if (st != FA_OK) return st;
+  return run_bwd(kUnused, kUnused, kUnused, o, dout, lse, nullptr, nullptr, nullptr, B, H, N, d,
+                 1.0f, 0, nullptr, 0.0f, 0, workspace, fa::kBwdPre, stream);
+}
+
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
+                      void* dv, int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                      const int32_t* key_lens, float dropout_p, uint64_t seed,
+                      const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const fa_status st = check_bwd({q, k, v, dout, dk, dv}, key_lens, B, H, N, d, dtype, scale,
+                                 dropout_p, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  return run_bwd(q, k, v, kUnused, dout, (const float*)kUnused, nullptr, dk, dv, B, H, N, d, scale,
+                 causal, key_lens, dropout_p, seed, (void*)workspace, fa::kBwdKV, stream);
+}
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B,
+                    int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                    const int32_t* key_lens, float dropout_p, uint64_t seed, const void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  const fa_status st = check_bwd({q, k, v, dout, dq}, key_lens, B, H, N, d, dtype, scale, dropout_p,
+                                 workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  return run_bwd(q, k, v, kUnused, dout, (const float*)kUnused, dq, nullptr, nullptr, B, H, N, d,
+                 scale, causal, key_lens, dropout_p, seed, (void*)workspace, fa::kBwdQ, stream);
 }
 
 }  // extern "C"

@@ -620,35 +620,45 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
 }
 
 template <int D, bool CAUSAL, bool DROPOUT>
-hipError_t launch_main(BwdParams p, int heads, hipStream_t s) {
-  p.num_blocks = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROPOUT>), dim3(heads * p.num_blocks),
-                     dim3(KvCfg<D>::THREADS), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  p.num_blocks = (p.N + QCfg<D>::BM - 1) / QCfg<D>::BM;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROPOUT>), dim3(heads * p.num_blocks),
-                     dim3(QCfg<D>::THREADS), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_main(BwdParams p, int heads, int stages, hipStream_t s) {
+  if (stages & kBwdKV) {
+    p.num_blocks = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROPOUT>), dim3(heads * p.num_blocks),
+                       dim3(KvCfg<D>::THREADS), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kBwdQ) {
+    p.num_blocks = (p.N + QCfg<D>::BM - 1) / QCfg<D>::BM;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROPOUT>), dim3(heads * p.num_blocks),
+                       dim3(QCfg<D>::THREADS), 0, s, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <int D>
-hipError_t run(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
-  const int64_t rows = (int64_t)a.B * a.H * a.N;
-  const int64_t pre_threads = rows * (D / 8);
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, s,
-                     (const bf16*)a.o, (const bf16*)a.dout, a.lse, a.delta, a.lse2, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t run(const BwdArgs& a, const BwdParams& p, int stages, hipStream_t s) {
+  if (stages & kBwdPre) {
+    const int64_t rows = (int64_t)a.B * a.H * a.N;
+    const int64_t pre_threads = rows * (D / 8);
+    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0,
+                       s, (const bf16*)a.o, (const bf16*)a.dout, a.lse, a.delta, a.lse2, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int heads = a.B * a.H;
   const bool drop = a.dropout_p > 0.0f;
-  if (a.causal) return drop ? launch_main<D, true, true>(p, heads, s) : launch_main<D, true, false>(p, heads, s);
-  return drop ? launch_main<D, false, true>(p, heads, s) : launch_main<D, false, false>(p, heads, s);
+  if (a.causal)
+    return drop ? launch_main<D, true, true>(p, heads, stages, s)
+                : launch_main<D, true, false>(p, heads, stages, s);
+  return drop ? launch_main<D, false, true>(p, heads, stages, s)
+              : launch_main<D, false, false>(p, heads, stages, s);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
   BwdParams p;
   p.q = (const bf16*)a.q;
   p.k = (const bf16*)a.k;
@@ -669,7 +679,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   p.drop_scale = a.drop_scale;
   p.seed_lo = (uint32_t)(a.seed & 0xffffffffu);
   p.seed_hi = (uint32_t)(a.seed >> 32);
-  return a.d == 64 ? run<64>(a, p, s) : run<128>(a, p, s);
+  return a.d == 64 ? run<64>(a, p, stages, s) : run<128>(a, p, stages, s);
 }
 
 }  // namespace fa

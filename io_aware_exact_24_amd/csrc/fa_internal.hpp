@@ -48,6 +48,9 @@ struct BwdArgs {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+// Backward stages, selected by a bit mask: the per-row preprocessing (D and
+// LSE*log2e into the workspace), the dK/dV kernel and the dQ kernel.
+enum : int { kBwdPre = 1, kBwdKV = 2, kBwdQ = 4, kBwdAll = 7 };
+hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
 
 }  // namespace fa

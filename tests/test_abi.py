@@ -113,3 +113,47 @@ def test_workspace_size_is_linear_in_n():
     assert ws(1, 1, 128, 96) == 0
     assert ws(1, 1, 128, 64, binding.FA_F32) == 0
     assert ws(0, 1, 128, 64) == 0
+
+
+def stage_calls(lib, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, scale=0.125, p=0.0, ws=P,
+                ws_bytes=None, null=None):
+    """The three backward stages with placeholder pointers; `null` names one
+    tensor argument to pass as NULL."""
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d, dtype)
+
+    def t(name):
+        return None if name == null else P
+
+    return {
+        "preprocess": lib.fa_bwd_preprocess(t("o"), t("dout"), t("lse"), B, H, N, d, dtype, ws,
+                                            ws_bytes, None),
+        "dkdv": lib.fa_bwd_dkdv(t("q"), t("k"), t("v"), t("dout"), t("dk"), t("dv"), B, H, N, d,
+                                dtype, scale, 0, None, p, 0, ws, ws_bytes, None),
+        "dq": lib.fa_bwd_dq(t("q"), t("k"), t("v"), t("dout"), t("dq"), B, H, N, d, dtype, scale, 0,
+                            None, p, 0, ws, ws_bytes, None),
+    }
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=0), INVALID), (dict(N=-3), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(dtype=binding.FA_F32), UNSUPPORTED), (dict(dtype=9), INVALID),
+    (dict(ws=None), INVALID), (dict(ws=P + 4), INVALID), (dict(ws_bytes=0), INVALID),
+])
+def test_backward_stages_reject(lib, kw, expect):
+    assert set(stage_calls(lib, **kw).values()) == {expect}
+
+
+@pytest.mark.parametrize("kw", [dict(scale=float("nan")), dict(scale=0.0), dict(p=1.0)])
+def test_backward_compute_stages_check_scale_and_dropout(lib, kw):
+    got = stage_calls(lib, **kw)
+    assert got["dkdv"] == INVALID and got["dq"] == INVALID
+
+
+@pytest.mark.parametrize("name,stage", [
+    ("o", "preprocess"), ("dout", "preprocess"), ("lse", "preprocess"),
+    ("q", "dkdv"), ("k", "dkdv"), ("v", "dkdv"), ("dout", "dkdv"), ("dk", "dkdv"), ("dv", "dkdv"),
+    ("q", "dq"), ("k", "dq"), ("v", "dq"), ("dout", "dq"), ("dq", "dq"),
+])
+def test_backward_stages_reject_null(lib, name, stage):
+    assert stage_calls(lib, null=name)[stage] == INVALID
