@@ -74,26 +74,36 @@ __device__ __forceinline__ float dropout_z(const BwdParams& p, int row, int key,
 // ----------------------------------------------------------------------------
 template <int D>
 struct KvCfg {
-  static constexpr int NW = 4;
+  static constexpr int NW = 8;        // two waves per SIMD
   static constexpr int THREADS = 64 * NW;
-  static constexpr int BK = 32 * NW;  // keys per workgroup
-  static constexpr int BQ = 64;       // query rows per tile
+  static constexpr int BK = 128;      // keys per workgroup: 4 groups of 32
+  static constexpr int BQ = 64;       // query rows per tile: 2 halves of 32
   static constexpr int CHUNKS = D / 8;
   static constexpr int TILE = BQ * D;                  // elements of a Q or dO tile
+  static constexpr int KTILE = BK * D;                 // elements of the K or V block
   static constexpr int LOADS = BQ * CHUNKS / THREADS;  // 16-byte copies per thread per tile
+  static constexpr int KLOADS = BK * CHUNKS / THREADS;
   static_assert(LOADS * THREADS == BQ * CHUNKS, "tile/thread mismatch");
+  static_assert(KLOADS * THREADS == BK * CHUNKS, "block/thread mismatch");
 };
 
+// Wave w owns key group w % 4 (32 keys) and row half w / 4 of every query
+// tile, so the two waves of a key group split the contraction over rows; their
+// partial dK^T / dV^T are added through LDS once at the end.  K and V of the
+// block stay in LDS (B operands of S and dP), which keeps a wave within 256
+// registers and lets two waves share each SIMD: one wave's exponentials and
+// packing run while the other's MFMAs do.
 template <int D, bool CAUSAL, bool DROPOUT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p) {
   using C = KvCfg<D>;
-  constexpr int BQ = C::BQ, NW = C::NW, TILE = C::TILE, BK = C::BK;
+  constexpr int BQ = C::BQ, NW = C::NW, TILE = C::TILE, BK = C::BK, KTILE = C::KTILE;
   constexpr int KC = D / 16;  // k-steps of the S and dP products
   constexpr int DU = D / 32;  // 32-wide blocks of the head dimension
-  // Stages of the Q and dO tiles and of the per-row LSE*log2e and D.
-  // Separate objects let the compiler see that a copy into one stage cannot
-  // alias reads of the other.
+  // K and V of the block; stages of the Q and dO tiles and of the per-row
+  // LSE*log2e and D.  Separate objects let the compiler see that a copy into
+  // one stage cannot alias reads of the other.
+  __shared__ __attribute__((aligned(1024))) bf16 skv[2 * KTILE];  // K block, then V block
   __shared__ __attribute__((aligned(1024))) bf16 sq0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 sq1[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 so0[TILE];
@@ -103,6 +113,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float sd0[BQ];
   __shared__ __attribute__((aligned(256))) float sd1[BQ];
 
+  bf16* const sk = skv;
+  bf16* const sv = skv + KTILE;
+
   const int N = p.N;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int head = lid / p.num_blocks;
@@ -110,17 +123,15 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int bi = head / p.H, hi = head - bi * p.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3, rh = wave >> 2;  // key group, row half
   const int li = lane & 31, hh = lane >> 5;
-  const int kb = jb * BK;         // first key of the workgroup
-  const int kw = kb + 32 * wave;  // first key of this wave
-  const int key = kw + li;        // this lane's key (column of S)
+  const int kb = jb * BK;               // first key of the workgroup
+  const int key = kb + 32 * kg + li;    // this lane's key (column of S)
 
   int L = N;
   if (p.key_lens) L = min(max(p.key_lens[bi], 0), N);
 
   const size_t head_off = (size_t)head * N * D;
-  const bf16* __restrict__ kg = p.k + head_off;
-  const bf16* __restrict__ vg = p.v + head_off;
 
   // Epilogue layout: dV^T / dK^T tile u, register r -> d = 32u + 8(r/4) + 4hh + r%4.
   f32x16 dkacc[DU], dvacc[DU];
@@ -132,7 +143,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       dvacc[u][r] = 0.0f;
     }
   auto store_dkdv = [&]() {
-    if (key >= N) return;
+    if (rh != 0 || key >= N) return;
     bf16* dkrow = p.dk + head_off + (size_t)key * D;
     bf16* dvrow = p.dv + head_off + (size_t)key * D;
 #pragma unroll
@@ -154,34 +165,29 @@ void bwd_dkdv_kernel(BwdParams p) {
     return;
   }
 
-  // K and V rows of this lane's key as B operands (k = head dimension).
-  bf16x8 kreg[KC], vreg[KC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    if (key < N) {
-      kreg[c] = *(const bf16x8*)(kg + (size_t)key * D + 16 * c + 8 * hh);
-      vreg[c] = *(const bf16x8*)(vg + (size_t)key * D + 16 * c + 8 * hh);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kreg[c][e] = (bf16)0.0f;
-        vreg[c][e] = (bf16)0.0f;
-      }
-    }
-  }
-
-  // Per-tile copies: Q and dO tiles, LSE*log2e and D rows.
+  // Copies: the K and V block once, then Q and dO tiles with LSE*log2e and D.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q + head_off, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.dout + head_off, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lse2 + (size_t)head * N, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.delta + (size_t)head * N, (uint32_t)N * 4);
-  uint32_t ld_off[C::LOADS];
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
+  // Byte offset within a tile of this lane's i-th 16-byte copy (the chunk
+  // slot it fills is (i * NW + wave) * 64 + lane).
+  auto copy_off = [&](int i) {
     const int pch = (i * NW + wave) * 64 + lane;
     const int r = pch / C::CHUNKS, pc = pch % C::CHUNKS;
-    ld_off[i] = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
+    return (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
+  };
+#pragma unroll
+  for (int i = 0; i < C::KLOADS; ++i) {
+    const uint32_t off = copy_off(i) + (uint32_t)kb * (D * 2);
+    lds_dma16(krs, sk + (i * NW + wave) * 512, off);
+    lds_dma16(vrs, sv + (i * NW + wave) * 512, off);
   }
+  uint32_t ld_off[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) ld_off[i] = copy_off(i);
   auto issue_tile = [&](int it, auto par_t) {
     constexpr int S = decltype(par_t)::value;
     bf16* qd = S ? sq1 : sq0;
@@ -202,12 +208,17 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // LDS element offsets of the operand reads (relative to a tile base).
-  // Row reads (A operand of S and dP): row 32a + li, logical chunk 2c + hh.
+  // LDS element offsets of the operand reads; the wave's row half and key
+  // group are folded in so that every stage and block base is a constant.
+  // Row reads (A operand Q / dO of S and dP: row 32rh + li of a tile; B
+  // operand K / V: row 32kg + li of the block), logical chunk 2c + hh.
   const int rsw = swz<D>(li);
-  int roff[KC];
+  int roffq[KC], roffk[KC];
 #pragma unroll
-  for (int c = 0; c < KC; ++c) roff[c] = li * D + (((2 * c + hh) ^ rsw) * 8);
+  for (int c = 0; c < KC; ++c) {
+    roffq[c] = (32 * rh + li) * D + (((2 * c + hh) ^ rsw) * 8);
+    roffk[c] = (32 * kg + li) * D + (((2 * c + hh) ^ rsw) * 8);
+  }
   // Transposing reads (A operand of dV^T and dK^T): within a 16-row chunk,
   // rows trow and trow + 8, columns tcol .. tcol + 3 of a 32-column block; the
   // k-slot e of a lane is row 8(e/4) + 4hh + e%4 of the chunk, which matches
@@ -221,8 +232,9 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
       const int r = trow + 8 * half;
-      toff[half][u] = r * D + (((4 * u + (tcol >> 3)) ^ swz<D>(r)) * 8) + (tcol & 7);
+      toff[half][u] = (32 * rh + r) * D + (((4 * u + (tcol >> 3)) ^ swz<D>(r)) * 8) + (tcol & 7);
     }
+  const int rowoff = 32 * rh + 4 * hh;  // per-row terms: rows 32rh + 8g + 4hh + e of a tile
 
   const float c2 = p.scale_log2;
   const int it0 = CAUSAL ? kb / BQ : 0;
@@ -240,101 +252,105 @@ void bwd_dkdv_kernel(BwdParams p) {
     const bf16* os = S ? so1 : so0;
     const float* ls = S ? sl1 : sl0;
     const float* dls = S ? sd1 : sd0;
-    const int r0 = it * BQ;
+    const int r0 = it * BQ + 32 * rh;  // first row of this wave
     __syncthreads();  // tile it resident in stage S; every wave is done with tile it-1
     // copies for the next tile go into the other stage, read during tile it-1
     if (it + 1 < nit) issue_tile(it + 1, std::integral_constant<int, S ^ 1>{});
 
-    // ---- S = Q K^T and dP = dO V^T: row tile a, k-step c; A from row reads.
-    f32x16 sacc[2], pacc[2];
+    // ---- S = Q K^T and dP = dO V^T (32 rows x 32 keys each), k-step c:
+    // A from Q / dO row reads, B from K / V row reads.
+    f32x16 sacc, pacc;
     const f32x16 zero = {};
-    constexpr int NS = 4 * KC;  // S0, S1, dP0, dP1 MFMAs
-    bf16x8 ring[3];
-    auto sread = [&](int i) {
-      const int m = i / KC, c = i % KC;  // m: 0,1 = S row tiles, 2,3 = dP row tiles
-      return *(const bf16x8*)((m < 2 ? qs : os) + roff[c] + (m & 1) * 32 * D);
-    };
-    ring[0] = sread(0);
-    ring[1] = sread(1);
+    constexpr int NS = 2 * KC;  // S then dP MFMAs
+    bf16x8 ra[3], rb[3];
+    auto aread = [&](int i) { return *(const bf16x8*)((i < KC ? qs : os) + roffq[i % KC]); };
+    auto bread = [&](int i) { return *(const bf16x8*)((i < KC ? sk : sv) + roffk[i % KC]); };
+    ra[0] = aread(0);
+    rb[0] = bread(0);
+    ra[1] = aread(1);
+    rb[1] = bread(1);
     __builtin_amdgcn_sched_barrier(0);
 
-    bf16x8 pb[4], dsb[4];  // P~ and dS as B operands, chunk kc = 16 rows
-    // P of S tile a, rows 32a + 8g + 4hh + e (e = 0..3), in place.
-    auto p_elems = [&](int a, int g) {
-      const f32x4 l4 = *(const f32x4*)(ls + 32 * a + 8 * g + 4 * hh);
+    bf16x8 pb[2], dsb[2];  // P~ and dS as B operands, chunk kc = 16 rows
+    // P of row group g (rows 8g + 4hh + e of the wave's 32), in place.
+    auto p_elems = [&](int g) {
+      const f32x4 l4 = *(const f32x4*)(ls + rowoff + 8 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float pv = fast_exp2(fmaf(sacc[a][4 * g + e], c2, -l4[e]));
+        float pv = fast_exp2(fmaf(sacc[4 * g + e], c2, -l4[e]));
         if constexpr (MASKED) {
-          const int row = r0 + 32 * a + 8 * g + 4 * hh + e;
+          const int row = r0 + 8 * g + 4 * hh + e;
           const bool ok = key < L && (!CAUSAL || key <= row);
           pv = ok ? pv : 0.0f;
         }
-        sacc[a][4 * g + e] = pv;
+        sacc[4 * g + e] = pv;
       }
     };
-    // dS (and P~ = P*Z) of row group g of tile a, packed into the B chunks.
-    auto ds_elems = [&](int a, int g) {
-      const f32x4 d4 = *(const f32x4*)(dls + 32 * a + 8 * g + 4 * hh);
+    // dS (and P~ = P*Z) of row group g, packed into the B chunks.
+    auto ds_elems = [&](int g) {
+      const f32x4 d4 = *(const f32x4*)(dls + rowoff + 8 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
-        const float pv = sacc[a][r];
-        float dp = pacc[a][r], pt = pv;
+        const float pv = sacc[r];
+        float dp = pacc[r], pt = pv;
         if constexpr (DROPOUT) {
-          const float z = dropout_z(p, r0 + 32 * a + 8 * g + 4 * hh + e, key, hi, bi);
+          const float z = dropout_z(p, r0 + 8 * g + 4 * hh + e, key, hi, bi);
           pt = pv * z;
           dp = dp * z;
         }
-        // chunk kc = 2a + g/2 holds rows 16kc + 8(x/4) + 4hh + x%4 in slot x
-        pb[2 * a + (g >> 1)][4 * (g & 1) + e] = (bf16)pt;
-        dsb[2 * a + (g >> 1)][4 * (g & 1) + e] = (bf16)(pv * (dp - d4[e]));
+        // chunk kc = g/2 holds rows 16kc + 8(x/4) + 4hh + x%4 in slot x
+        pb[g >> 1][4 * (g & 1) + e] = (bf16)pt;
+        dsb[g >> 1][4 * (g & 1) + e] = (bf16)(pv * (dp - d4[e]));
       }
     };
-    // MFMA i plus its share of the elementwise work:
-    //   S0 | S1 + P of tile 0 | dP0 + P of tile 1 | dP1 + dS of tile 0,
-    // one 4-row group every KC/4 MFMAs.
+    // MFMA i plus its share of the elementwise work: the exponentials of S
+    // while dP is computed, one 4-row group every KC/4 MFMAs.
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      if (i + 2 < NS) ring[(i + 2) % 3] = sread(i + 2);
-      const int m = i / KC, c = i % KC;
-      f32x16& acc = m < 2 ? sacc[m & 1] : pacc[m & 1];
-      acc = mfma32(ring[i % 3], m < 2 ? kreg[c] : vreg[c], c == 0 ? zero : acc);
-      if ((c * 4) % KC == 0) {
-        const int g = c * 4 / KC;
-        if (m == 1) p_elems(0, g);
-        if (m == 2) p_elems(1, g);
-        if (m == 3) ds_elems(0, g);
+      if (i + 2 < NS) {
+        ra[(i + 2) % 3] = aread(i + 2);
+        rb[(i + 2) % 3] = bread(i + 2);
       }
+      const int c = i % KC;
+      f32x16& acc = i < KC ? sacc : pacc;
+      acc = mfma32(ra[i % 3], rb[i % 3], c == 0 ? zero : acc);
+      if (i >= KC && (c * 4) % KC == 0) p_elems(c * 4 / KC);
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- dV^T += dO^T P~ and dK^T += Q^T dS (contraction over the 64 rows);
-    // the dS of row tile 1 is finished during the first dV^T MFMAs.
+    // ---- dV^T += dO^T P~ and dK^T += Q^T dS (contraction over the wave's 32
+    // rows); dS is finished during the first dV^T MFMAs.
     const lds_bf16* qt = to_lds(qs);
     const lds_bf16* ot = to_lds(os);
-    constexpr int NT = 8 * DU;  // dV^T then dK^T MFMAs: index = (which, kc, u)
+    constexpr int NT = 4 * DU;  // dV^T then dK^T MFMAs: index = (which, kc, u)
     auto tnext = [&](int i) {
-      const int which = i / (4 * DU), kc = (i / DU) % 4, u = i % DU;
+      const int which = i / (2 * DU), kc = (i / DU) % 2, u = i % DU;
       const lds_bf16* base = which == 0 ? ot : qt;
       const bf16x4 lo = lds_read_tr4(base + toff[0][u] + 16 * kc * D);
       const bf16x4 h4 = lds_read_tr4(base + toff[1][u] + 16 * kc * D);
       return bf16x8{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
     };
-    ring[0] = tnext(0);
-    ring[1] = tnext(1);
+    ra[0] = tnext(0);
+    ra[1] = tnext(1);
     __builtin_amdgcn_sched_barrier(0);
+    // P~ and dS groups 0, 1 form chunk 0, used from MFMA 0.
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      if (i + 2 < NT) ring[(i + 2) % 3] = tnext(i + 2);
-      const int which = i / (4 * DU), kc = (i / DU) % 4, u = i % DU;
-      if (which == 0) {
-        dvacc[u] = mfma32(ring[i % 3], pb[kc], dvacc[u]);
-      } else {
-        dkacc[u] = mfma32(ring[i % 3], dsb[kc], dkacc[u]);
+      if (i == 0) {
+        ds_elems(0);
+        ds_elems(1);
       }
-      // chunks 2, 3 (row tile 1) are first used by dV^T MFMA 2*DU
-      if (i < 4) ds_elems(1, i);
+      if (i + 2 < NT) ra[(i + 2) % 3] = tnext(i + 2);
+      const int which = i / (2 * DU), kc = (i / DU) % 2, u = i % DU;
+      if (which == 0) {
+        dvacc[u] = mfma32(ra[i % 3], pb[kc], dvacc[u]);
+      } else {
+        dkacc[u] = mfma32(ra[i % 3], dsb[kc], dkacc[u]);
+      }
+      // groups 2, 3 (chunk 1) are first used by MFMA DU
+      if (i == 1) ds_elems(2);
+      if (i == DU - 1) ds_elems(3);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmem();  // next tile landed (this wave's share) before the next barrier
@@ -358,6 +374,30 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
   if (it < nit) iter(it, P0{}, F_{});
 
+  // Add the row-half-1 partials into the row-half-0 waves through LDS (the
+  // K/V block buffer is free now), dK^T then dV^T: register r of tile u of
+  // lane l at (u*16 + r)*64 + l of the key group's slot.
+  float* const xs = (float*)skv;
+  static_assert(4 * D / 32 * 16 * 64 * 4 <= 2 * KTILE * 2, "exchange must fit the K/V buffer");
+  float* const mine = xs + kg * (DU * 16 * 64);
+  auto exchange = [&](f32x16 (&acc)[DU]) {
+    __syncthreads();
+    if (rh == 1) {
+#pragma unroll
+      for (int u = 0; u < DU; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[(u * 16 + r) * 64 + lane] = acc[u][r];
+    }
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+      for (int u = 0; u < DU; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[u][r] += mine[(u * 16 + r) * 64 + lane];
+    }
+  };
+  exchange(dkacc);
+  exchange(dvacc);
   store_dkdv();
 }
 
