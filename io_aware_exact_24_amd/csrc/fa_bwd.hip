@@ -103,7 +103,6 @@ void bwd_dkdv_kernel(BwdParams p) {
   // K and V of the block; stages of the Q and dO tiles and of the per-row
   // LSE*log2e and D.  Separate objects let the compiler see that a copy into
   // one stage cannot alias reads of the other.
-  __shared__ __attribute__((aligned(1024))) bf16 skv[2 * KTILE];  // K block, then V block
   __shared__ __attribute__((aligned(1024))) bf16 sq0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 sq1[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 so0[TILE];
@@ -112,6 +111,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float sl1[BQ];
   __shared__ __attribute__((aligned(256))) float sd0[BQ];
   __shared__ __attribute__((aligned(256))) float sd1[BQ];
+  __shared__ __attribute__((aligned(1024))) bf16 skv[2 * KTILE];  // K block, then V block
 
   bf16* const sk = skv;
   bf16* const sv = skv + KTILE;
