@@ -50,8 +50,7 @@
  *                       element count overflows int64, non-finite or
  *                       non-positive scale, p outside [0, 1), workspace NULL
  *                       or smaller than fa_bwd_workspace_size().
- *   FA_ERR_UNSUPPORTED  d not in {64, 128}; fp32 with dropout, causal masking,
- *                       key lengths or d != 64 ... (see fa_fwd); fp32 backward.
+ *   FA_ERR_UNSUPPORTED  d not in {64, 128}; fp32 with dropout; fp32 backward.
  *   FA_ERR_HIP          a launch failed (hipGetLastError after launching).
  * key_lens lives in device memory and cannot be range-checked on the host; the
  * kernels clamp each L_b into [0, N].
@@ -93,9 +92,9 @@ typedef enum {
  *   seed      Philox key, used only when dropout_p > 0.
  *
  * dtype FA_BF16: d in {64, 128}, every mask and dropout combination.
- * dtype FA_F32:  d == 64, no causal mask, no key_lens, no dropout
- *                (the single-head fp32 workload); anything else returns
- *                FA_ERR_UNSUPPORTED.
+ * dtype FA_F32:  d in {64, 128}, causal mask and key_lens allowed, no
+ *                dropout (FA_ERR_UNSUPPORTED).  A simple kernel meant for the
+ *                small single-head fp32 workload, not tuned for large sizes.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
