@@ -20,6 +20,9 @@ OUT = os.path.join(PKG, "libfa.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+# The dK/dV kernel keeps its long-lived accumulators in AccVGPRs through inline
+# assembly; every other MFMA must write ordinary VGPRs, which the VALU reads.
+EXTRA = {"fa_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -35,7 +38,7 @@ COMMON = [
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

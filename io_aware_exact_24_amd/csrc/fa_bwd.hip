@@ -10,13 +10,15 @@
 //
 // Three kernels on one stream:
 //  1. bwd_pre:  D_i and LSE_i * log2(e) per row (fp32, in the workspace).
-//  2. bwd_dkdv: one workgroup of 4 waves per 128-key block; each wave owns 32
-//     keys and keeps their K and V rows (B operands) and fp32 dK^T / dV^T
-//     accumulators in registers while the workgroup walks the 64-row query
-//     tiles that can see the block.  S and dP come out of the MFMA with a lane
-//     per key and 16 query rows per lane, which is the B-operand layout of the
-//     dV^T and dK^T products; their A operands dO^T and Q^T are transposing
-//     LDS reads of the row-major tiles.
+//  2. bwd_dkdv: one workgroup of 4 waves (one per SIMD) per 128-key block;
+//     each wave owns 32 keys and keeps their K and V rows (B operands) and the
+//     fp32 dK^T / dV^T accumulators (in AccVGPRs) in registers while the
+//     workgroup walks the 64-row query tiles that can see the block.  S and
+//     dP come out of the MFMA with a lane per key and 16 query rows per lane,
+//     which is the B-operand layout of the dV^T and dK^T products; their A
+//     operands dO^T and Q^T are transposing LDS reads of the row-major tiles.
+//     The products of tile t are skewed against those of tile t+1 so every
+//     group of MFMAs has independent elementwise work beside it.
 //  3. bwd_dq: one workgroup of 4 waves x 32 queries per query block; each
 //     wave keeps Q^T, dO^T and an fp32 dQ^T accumulator in registers and
 //     streams K/V tiles, recomputing S^T and dP^T (a lane per query, so LSE
@@ -27,9 +29,9 @@
 // in L2), no fp32 dQ workspace and no conversion pass, and dQ is
 // deterministic.
 //
-// Q/dO tiles (bwd_dkdv) and K/V tiles (bwd_dq) are copied global -> LDS by
-// buffer loads into double-buffered, XOR-swizzled stages (conflict-free row and
-// transposing reads, rows past N read as zero).
+// Q/dO tiles (bwd_dkdv, three stages) and K/V tiles (bwd_dq, two stages) are
+// copied global -> LDS by buffer loads into XOR-swizzled stages (conflict-free
+// row and transposing reads, rows past N read as zero).
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -74,47 +76,77 @@ __device__ __forceinline__ float dropout_z(const BwdParams& p, int row, int key,
 // ----------------------------------------------------------------------------
 template <int D>
 struct KvCfg {
-  static constexpr int NW = 8;        // two waves per SIMD
+  static constexpr int NW = 4;        // one wave per SIMD
   static constexpr int THREADS = 64 * NW;
-  static constexpr int BK = 128;      // keys per workgroup: 4 groups of 32
+  static constexpr int BK = 32 * NW;  // keys per workgroup: a 32-key group per wave
   static constexpr int BQ = 64;       // query rows per tile: 2 halves of 32
   static constexpr int CHUNKS = D / 8;
   static constexpr int TILE = BQ * D;                  // elements of a Q or dO tile
-  static constexpr int KTILE = BK * D;                 // elements of the K or V block
   static constexpr int LOADS = BQ * CHUNKS / THREADS;  // 16-byte copies per thread per tile
-  static constexpr int KLOADS = BK * CHUNKS / THREADS;
   static_assert(LOADS * THREADS == BQ * CHUNKS, "tile/thread mismatch");
-  static_assert(KLOADS * THREADS == BK * CHUNKS, "block/thread mismatch");
 };
 
-// Wave w owns key group w % 4 (32 keys) and row half w / 4 of every query
-// tile, so the two waves of a key group split the contraction over rows; their
-// partial dK^T / dV^T are added through LDS once at the end.  K and V of the
-// block stay in LDS (B operands of S and dP), which keeps a wave within 256
-// registers and lets two waves share each SIMD: one wave's exponentials and
-// packing run while the other's MFMAs do.
+template <int S>
+using Stage = std::integral_constant<int, S % 3>;
+
+// Keep decision of element (row, key) for dropout.
+__device__ __forceinline__ bool dropout_keep(const BwdParams& p, int row, int key, int hi, int bi) {
+  const u32x4 w = philox((uint32_t)key >> 2, (uint32_t)row, (uint32_t)hi, (uint32_t)bi, p.seed_lo,
+                         p.seed_hi);
+  const uint32_t word = (key & 3) == 0 ? w[0] : (key & 3) == 1 ? w[1] : (key & 3) == 2 ? w[2] : w[3];
+  return word >= p.drop_threshold;
+}
+
+// One wave per SIMD, each owning 32 keys of the block: their K and V rows
+// are B operands held in registers and their dK^T / dV^T accumulators stay
+// in registers for the whole walk over the 64-row query tiles.  The work of
+// tile t is skewed against tile t+1 so that every group of MFMAs has
+// independent elementwise work beside it:
+//   phase 0: dV^T += dO_t^T P~_t      | dS_t of rows 0..31
+//   phase 1: S_{t+1} = Q_{t+1} K^T    | dS_t of rows 32..63
+//   phase 2: dK^T += Q_t^T dS_t       | P_{t+1} of rows 0..31
+//   phase 3: dP_{t+1} = dO_{t+1} V^T  | P_{t+1} of rows 32..63
+// Tiles t (transposing reads) and t+1 (row reads) are read while tile t+2 is
+// copied, so Q, dO, LSE*log2e and D have three LDS stages.
 template <int D, bool CAUSAL, bool DROPOUT>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p) {
   using C = KvCfg<D>;
-  constexpr int BQ = C::BQ, NW = C::NW, TILE = C::TILE, BK = C::BK, KTILE = C::KTILE;
+  constexpr int BQ = C::BQ, NW = C::NW, TILE = C::TILE, BK = C::BK;
   constexpr int KC = D / 16;  // k-steps of the S and dP products
   constexpr int DU = D / 32;  // 32-wide blocks of the head dimension
-  // K and V of the block; stages of the Q and dO tiles and of the per-row
-  // LSE*log2e and D.  Separate objects let the compiler see that a copy into
-  // one stage cannot alias reads of the other.
+  constexpr int NP = 2 * KC;  // MFMAs per phase (also 4 * DU)
+  static_assert(NP == 4 * DU, "phase sizes");
+  constexpr int PD = 4;       // operand reads run PD MFMAs ahead
+  constexpr int RG = 8;       // ring slots (divides every body's MFMA count)
   __shared__ __attribute__((aligned(1024))) bf16 sq0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sq1[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 so0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sq1[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 so1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sq2[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 so2[TILE];
   __shared__ __attribute__((aligned(256))) float sl0[BQ];
   __shared__ __attribute__((aligned(256))) float sl1[BQ];
+  __shared__ __attribute__((aligned(256))) float sl2[BQ];
   __shared__ __attribute__((aligned(256))) float sd0[BQ];
   __shared__ __attribute__((aligned(256))) float sd1[BQ];
-  __shared__ __attribute__((aligned(1024))) bf16 skv[2 * KTILE];  // K block, then V block
-
-  bf16* const sk = skv;
-  bf16* const sv = skv + KTILE;
+  __shared__ __attribute__((aligned(256))) float sd2[BQ];
+  auto qst = [&](auto s) __attribute__((always_inline)) -> bf16* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? sq0 : S == 1 ? sq1 : sq2;
+  };
+  auto ost = [&](auto s) __attribute__((always_inline)) -> bf16* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? so0 : S == 1 ? so1 : so2;
+  };
+  auto lst = [&](auto s) __attribute__((always_inline)) -> float* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? sl0 : S == 1 ? sl1 : sl2;
+  };
+  auto dst = [&](auto s) __attribute__((always_inline)) -> float* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? sd0 : S == 1 ? sd1 : sd2;
+  };
 
   const int N = p.N;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -123,27 +155,23 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int bi = head / p.H, hi = head - bi * p.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kg = wave & 3, rh = wave >> 2;  // key group, row half
   const int li = lane & 31, hh = lane >> 5;
-  const int kb = jb * BK;               // first key of the workgroup
-  const int key = kb + 32 * kg + li;    // this lane's key (column of S)
+  const int kb = jb * BK;             // first key of the workgroup
+  const int key = kb + 32 * wave + li;  // this lane's key (column of S)
 
   int L = N;
   if (p.key_lens) L = min(max(p.key_lens[bi], 0), N);
 
   const size_t head_off = (size_t)head * N * D;
 
-  // Epilogue layout: dV^T / dK^T tile u, register r -> d = 32u + 8(r/4) + 4hh + r%4.
+  // dV^T / dK^T tile u, register r -> d = 32u + 8(r/4) + 4hh + r%4; the first
+  // product into each defines it.
   f32x16 dkacc[DU], dvacc[DU];
-#pragma unroll
-  for (int u = 0; u < DU; ++u)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dkacc[u][r] = 0.0f;
-      dvacc[u][r] = 0.0f;
-    }
-  auto store_dkdv = [&]() {
-    if (rh != 0 || key >= N) return;
+  // Keys past the key length take part in nothing: their gradients are zero.
+  // Their lanes compute unmasked values (each lane's columns of S, dP, dV^T
+  // and dK^T depend on its own key only), which the store discards.
+  auto store_dkdv = [&](bool zero) __attribute__((always_inline)) {
+    if (key >= N) return;
     bf16* dkrow = p.dk + head_off + (size_t)key * D;
     bf16* dvrow = p.dv + head_off + (size_t)key * D;
 #pragma unroll
@@ -153,76 +181,90 @@ void bwd_dkdv_kernel(BwdParams p) {
         bf16x4 kv, vv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kv[e] = (bf16)(dkacc[u][4 * g + e] * p.scale);
-          vv[e] = (bf16)dvacc[u][4 * g + e];
+          kv[e] = zero ? (bf16)0.0f : (bf16)(dkacc[u][4 * g + e] * p.scale);
+          vv[e] = zero ? (bf16)0.0f : (bf16)dvacc[u][4 * g + e];
         }
         *(bf16x4*)(dkrow + 32 * u + 8 * g + 4 * hh) = kv;
         *(bf16x4*)(dvrow + 32 * u + 8 * g + 4 * hh) = vv;
       }
   };
-  if (kb >= L) {  // every key of the block is padding: zero gradients
-    store_dkdv();
+  if (kb >= L) {  // every key of the block is padding
+    if (key < N) {
+      const bf16x4 z = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+#pragma unroll
+      for (int c = 0; c < D / 4; c += 2) {
+        *(bf16x4*)(p.dk + head_off + (size_t)key * D + 4 * c + 4 * hh) = z;
+        *(bf16x4*)(p.dv + head_off + (size_t)key * D + 4 * c + 4 * hh) = z;
+      }
+    }
     return;
   }
 
-  // Copies: the K and V block once, then Q and dO tiles with LSE*log2e and D.
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, (uint32_t)N * D * 2);
+  // K and V rows of this lane's key as B operands (k = head dimension).
+  bf16x8 kreg[KC], vreg[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    if (key < N) {
+      kreg[c] = *(const bf16x8*)(p.k + head_off + (size_t)key * D + 16 * c + 8 * hh);
+      vreg[c] = *(const bf16x8*)(p.v + head_off + (size_t)key * D + 16 * c + 8 * hh);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kreg[c][e] = (bf16)0.0f;
+        vreg[c][e] = (bf16)0.0f;
+      }
+    }
+  }
+
+  // Copies of Q and dO tiles with LSE*log2e and D (rows past N read as zero).
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q + head_off, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.dout + head_off, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lse2 + (size_t)head * N, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.delta + (size_t)head * N, (uint32_t)N * 4);
-  // Byte offset within a tile of this lane's i-th 16-byte copy (the chunk
-  // slot it fills is (i * NW + wave) * 64 + lane).
-  auto copy_off = [&](int i) {
-    const int pch = (i * NW + wave) * 64 + lane;
-    const int r = pch / C::CHUNKS, pc = pch % C::CHUNKS;
-    return (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
-  };
-#pragma unroll
-  for (int i = 0; i < C::KLOADS; ++i) {
-    const uint32_t off = copy_off(i) + (uint32_t)kb * (D * 2);
-    lds_dma16(krs, sk + (i * NW + wave) * 512, off);
-    lds_dma16(vrs, sv + (i * NW + wave) * 512, off);
+  // Copy i of this lane fills chunk slot (i * NW + wave) * 64 + lane: row
+  // r = (i * NW + wave) * 64 / CHUNKS + lane / CHUNKS, chunk lane % CHUNKS.
+  // The swizzle of r depends on r mod 16 only, which does not change with i,
+  // so copy i is copy 0 shifted by i * NW * 64 chunks.
+  static_assert((NW * 64 / C::CHUNKS) % 16 == 0, "copy rows must keep their swizzle");
+  uint32_t ld_off0;
+  {
+    const int r = wave * 64 / C::CHUNKS + lane / C::CHUNKS, pc = lane % C::CHUNKS;
+    ld_off0 = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
   }
-  uint32_t ld_off[C::LOADS];
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) ld_off[i] = copy_off(i);
-  auto issue_tile = [&](int it, auto par_t) {
-    constexpr int S = decltype(par_t)::value;
-    bf16* qd = S ? sq1 : sq0;
-    bf16* od = S ? so1 : so0;
-    const uint32_t base = (uint32_t)it * (BQ * D * 2);
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      lds_dma16(qrs, qd + (i * NW + wave) * 512, ld_off[i] + base);
-      lds_dma16(ors, od + (i * NW + wave) * 512, ld_off[i] + base);
-    }
-    // 64 rows of 4 bytes: one wave-wide 4-byte copy each (rows past N read 0)
-    if (wave == 0) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void_t*)(S ? sl1 : sl0), 4,
-                                               (uint32_t)(it * BQ + lane) * 4, 0, 0, 0);
-    } else if (wave == 1) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void_t*)(S ? sd1 : sd0), 4,
+  // Copy piece x of tile `it` into stage s: pieces 0 .. 2*LOADS-1 are this
+  // wave's Q and dO chunks, piece 2*LOADS the per-row values (waves 0-1 copy
+  // LSE*log2e, waves 2-3 copy D: duplicates of the same values, no branch).
+  // Tiles past the end read as zero.
+  constexpr int NPIECE = 2 * C::LOADS + 1;
+  auto issue_piece = [&](int it, auto s, auto x_t) __attribute__((always_inline)) {
+    constexpr int x = decltype(x_t)::value;
+    if constexpr (x < 2 * C::LOADS) {
+      constexpr int i = x / 2;
+      const uint32_t off = ld_off0 + (uint32_t)it * (BQ * D * 2) + (uint32_t)(i * NW * 64 * 16);
+      if constexpr (x % 2 == 0)
+        lds_dma16(qrs, qst(s) + (i * NW + wave) * 512, off);
+      else
+        lds_dma16(ors, ost(s) + (i * NW + wave) * 512, off);
+    } else {
+      const bool dv = wave >= 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(dv ? drs : lrs, (lds_void_t*)(dv ? dst(s) : lst(s)), 4,
                                                (uint32_t)(it * BQ + lane) * 4, 0, 0, 0);
     }
+  };
+  auto issue_tile = [&](int it, auto s) __attribute__((always_inline)) {
+    static_for<NPIECE>([&](auto x_t) __attribute__((always_inline)) { issue_piece(it, s, x_t); });
   };
 
-  // LDS element offsets of the operand reads; the wave's row half and key
-  // group are folded in so that every stage and block base is a constant.
-  // Row reads (A operand Q / dO of S and dP: row 32rh + li of a tile; B
-  // operand K / V: row 32kg + li of the block), logical chunk 2c + hh.
+  // LDS element offsets of the operand reads.  Row reads (A operand of S and
+  // dP): row 32a + li of a tile, logical chunk 2c + hh.  Transposing reads (A
+  // operand of dV^T and dK^T): within a 16-row chunk, rows trow and trow + 8,
+  // columns tcol .. tcol + 3 of a 32-column block; the k-slot x of a lane is
+  // row 8(x/4) + 4hh + x%4 of the chunk, the row order of P and dS in the MFMA
+  // output layout.
   const int rsw = swz<D>(li);
-  int roffq[KC], roffk[KC];
+  int roff[KC];
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    roffq[c] = (32 * rh + li) * D + (((2 * c + hh) ^ rsw) * 8);
-    roffk[c] = (32 * kg + li) * D + (((2 * c + hh) ^ rsw) * 8);
-  }
-  // Transposing reads (A operand of dV^T and dK^T): within a 16-row chunk,
-  // rows trow and trow + 8, columns tcol .. tcol + 3 of a 32-column block; the
-  // k-slot e of a lane is row 8(e/4) + 4hh + e%4 of the chunk, which matches
-  // the row order of P and dS in the MFMA output layout.
+  for (int c = 0; c < KC; ++c) roff[c] = li * D + (((2 * c + hh) ^ rsw) * 8);
   const int g16 = lane & 15;
   const int trow = 4 * hh + (g16 >> 2);
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
@@ -232,173 +274,222 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
       const int r = trow + 8 * half;
-      toff[half][u] = (32 * rh + r) * D + (((4 * u + (tcol >> 3)) ^ swz<D>(r)) * 8) + (tcol & 7);
+      toff[half][u] = r * D + (((4 * u + (tcol >> 3)) ^ swz<D>(r)) * 8) + (tcol & 7);
     }
-  const int rowoff = 32 * rh + 4 * hh;  // per-row terms: rows 32rh + 8g + 4hh + e of a tile
+  auto row_read = [&](const bf16* base, int a, int c) __attribute__((always_inline)) {
+    return *(const bf16x8*)(base + roff[c] + a * 32 * D);
+  };
+  auto tr_read = [&](const bf16* base, int kc, int u) __attribute__((always_inline)) {
+    const lds_bf16* b = to_lds(base);
+    const bf16x4 lo = lds_read_tr4(b + toff[0][u] + 16 * kc * D);
+    const bf16x4 h4 = lds_read_tr4(b + toff[1][u] + 16 * kc * D);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
+  };
+  // Per-row values of group g (rows 8g + 4hh .. +3) of row half a.
+  auto rows4 = [&](const float* base, int grp) __attribute__((always_inline)) {
+    return *(const f32x4*)(base + 8 * grp + 4 * hh);  // grp = 4a + g
+  };
 
   const float c2 = p.scale_log2;
   const int it0 = CAUSAL ? kb / BQ : 0;
   const int nit = (N + BQ - 1) / BQ;
-  // Tiles before it_free need masking: causal diagonal tiles, or all tiles of
-  // a block that reaches past the key length.
-  int it_free = it0;
-  if (CAUSAL) it_free = min(nit, (kb + BK - 1) / BQ + 1);
-  if (kb + BK > L) it_free = nit;
 
-  auto iter = [&](int it, auto par_t, auto masked_t) {
-    constexpr int S = decltype(par_t)::value;  // stage parity = (it - it0) & 1
+  // State carried from one tile to the next: P (fp32, masked), dP, P~ packed
+  // as B chunks (chunk kc holds rows 16kc + 8(x/4) + 4hh + x%4 in slot x), the
+  // dropout keep bits, and the operand ring.
+  f32x16 sp[2], sdp[2];
+  bf16x8 spb[4];
+  uint32_t zb = 0;
+  bf16x8 ring[RG];
+  const f32x16 zero = {};
+
+  // P of element pair (k, k+1) of tile `it` from its scores (in place in s),
+  // packed into pb; k = 16a + r, rows 32a + 8(r/4) + 4hh + r%4.
+  // Allowed iff the row offset within the tile is at least lo (and only then).
+  auto exp_pair = [&](int it, f32x16 (&s)[2], bf16x8 (&pb)[4], uint32_t& zn, int k,
+                      const f32x4& l4, int lo, auto masked_t) {
     constexpr bool MASKED = decltype(masked_t)::value;
-    const bf16* qs = S ? sq1 : sq0;
-    const bf16* os = S ? so1 : so0;
-    const float* ls = S ? sl1 : sl0;
-    const float* dls = S ? sd1 : sd0;
-    const int r0 = it * BQ + 32 * rh;  // first row of this wave
-    __syncthreads();  // tile it resident in stage S; every wave is done with tile it-1
-    // copies for the next tile go into the other stage, read during tile it-1
-    if (it + 1 < nit) issue_tile(it + 1, std::integral_constant<int, S ^ 1>{});
-
-    // ---- S = Q K^T and dP = dO V^T (32 rows x 32 keys each), k-step c:
-    // A from Q / dO row reads, B from K / V row reads.
-    f32x16 sacc, pacc;
-    const f32x16 zero = {};
-    constexpr int NS = 2 * KC;  // S then dP MFMAs
-    bf16x8 ra[3], rb[3];
-    auto aread = [&](int i) { return *(const bf16x8*)((i < KC ? qs : os) + roffq[i % KC]); };
-    auto bread = [&](int i) { return *(const bf16x8*)((i < KC ? sk : sv) + roffk[i % KC]); };
-    ra[0] = aread(0);
-    rb[0] = bread(0);
-    ra[1] = aread(1);
-    rb[1] = bread(1);
-    __builtin_amdgcn_sched_barrier(0);
-
-    bf16x8 pb[2], dsb[2];  // P~ and dS as B operands, chunk kc = 16 rows
-    // P of row group g (rows 8g + 4hh + e of the wave's 32), in place.
-    auto p_elems = [&](int g) {
-      const f32x4 l4 = *(const f32x4*)(ls + rowoff + 8 * g);
+    const int a = k >> 4, r = k & 15, g = r >> 2, e = r & 3;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float pv = fast_exp2(fmaf(sacc[4 * g + e], c2, -l4[e]));
-        if constexpr (MASKED) {
-          const int row = r0 + 8 * g + 4 * hh + e;
-          const bool ok = key < L && (!CAUSAL || key <= row);
-          pv = ok ? pv : 0.0f;
-        }
-        sacc[4 * g + e] = pv;
+    for (int x = 0; x < 2; ++x) {
+      float pv = fast_exp2(fmaf(s[a][r + x], c2, -l4[e + x]));
+      if constexpr (MASKED) pv = (32 * a + 8 * g + e + x) >= lo ? pv : 0.0f;
+      pin(pv);
+      s[a][r + x] = pv;
+      float pt = pv;
+      if constexpr (DROPOUT) {
+        const bool keep = dropout_keep(p, it * BQ + 32 * a + 8 * g + 4 * hh + e + x, key, hi, bi);
+        zn |= (uint32_t)keep << (k + x);
+        pt = keep ? pv * p.drop_scale : 0.0f;
       }
-    };
-    // dS (and P~ = P*Z) of row group g, packed into the B chunks.
-    auto ds_elems = [&](int g) {
-      const f32x4 d4 = *(const f32x4*)(dls + rowoff + 8 * g);
+      pb[2 * a + (g >> 1)][4 * (g & 1) + e + x] = (bf16)pt;
+    }
+    pin(pb[2 * a + (g >> 1)]);  // keep the work beside this MFMA
+  };
+  // Row-offset bound of the causal mask for tile `it` (see exp_pair).
+  auto mask_lo = [&](int it) __attribute__((always_inline)) { return key - it * BQ - 4 * hh; };
+  // dS of element pair (k, k+1) of the current tile into dsb.
+  auto ds_pair = [&](bf16x8 (&dsb)[4], int k, const f32x4& d4) {
+    const int a = k >> 4, r = k & 15, g = r >> 2, e = r & 3;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        const float pv = sacc[r];
-        float dp = pacc[r], pt = pv;
-        if constexpr (DROPOUT) {
-          const float z = dropout_z(p, r0 + 8 * g + 4 * hh + e, key, hi, bi);
-          pt = pv * z;
-          dp = dp * z;
-        }
-        // chunk kc = g/2 holds rows 16kc + 8(x/4) + 4hh + x%4 in slot x
-        pb[g >> 1][4 * (g & 1) + e] = (bf16)pt;
-        dsb[g >> 1][4 * (g & 1) + e] = (bf16)(pv * (dp - d4[e]));
-      }
+    for (int x = 0; x < 2; ++x) {
+      float dp = sdp[a][r + x];
+      if constexpr (DROPOUT) dp = ((zb >> (k + x)) & 1) ? dp * p.drop_scale : 0.0f;
+      dsb[2 * a + (g >> 1)][4 * (g & 1) + e + x] = (bf16)(sp[a][r + x] * (dp - d4[e + x]));
+    }
+    pin(dsb[2 * a + (g >> 1)]);  // keep the work beside this MFMA
+  };
+
+  // ---- prologue: tiles it0 (stage 0) and it0 + 1 (stage 1); S, dP and P of
+  // tile it0; the first operands of its body.
+  issue_tile(it0, Stage<0>{});
+  issue_tile(it0 + 1, Stage<1>{});
+  wait_vmem();
+  __syncthreads();
+  {
+    const bf16* q = qst(Stage<0>{});
+    const bf16* o = ost(Stage<0>{});
+    constexpr int NS = 2 * NP;  // S halves, then dP halves
+    auto pread = [&](int i) __attribute__((always_inline)) {
+      const int m = i / KC, c = i % KC;
+      return row_read(m < 2 ? q : o, m & 1, c);
     };
-    // MFMA i plus its share of the elementwise work: the exponentials of S
-    // while dP is computed, one 4-row group every KC/4 MFMAs.
+    bf16x8 pr[3];
+    pr[0] = pread(0);
+    pr[1] = pread(1);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      if (i + 2 < NS) {
-        ra[(i + 2) % 3] = aread(i + 2);
-        rb[(i + 2) % 3] = bread(i + 2);
-      }
-      const int c = i % KC;
-      f32x16& acc = i < KC ? sacc : pacc;
-      acc = mfma32(ra[i % 3], rb[i % 3], c == 0 ? zero : acc);
-      if (i >= KC && (c * 4) % KC == 0) p_elems(c * 4 / KC);
-      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < NS) pr[(i + 2) % 3] = pread(i + 2);
+      const int m = i / KC, c = i % KC;
+      f32x16& acc = m < 2 ? sp[m & 1] : sdp[m & 1];
+      acc = mfma32(pr[i % 3], m < 2 ? kreg[c] : vreg[c], c == 0 ? zero : acc);
     }
+    const float* ls = lst(Stage<0>{});
+    const int lo = mask_lo(it0);
+#pragma unroll
+    for (int k = 0; k < 32; k += 2) {
+      const f32x4 l4 = rows4(ls, k >> 2);
+      exp_pair(it0, sp, spb, zb, k, l4, lo, std::integral_constant<bool, CAUSAL>{});
+    }
+#pragma unroll
+    for (int i = 0; i < PD; ++i) ring[i] = tr_read(o, i / DU, i % DU);
+  }
 
-    // ---- dV^T += dO^T P~ and dK^T += Q^T dS (contraction over the wave's 32
-    // rows); dS is finished during the first dV^T MFMAs.
-    const lds_bf16* qt = to_lds(qs);
-    const lds_bf16* ot = to_lds(os);
-    constexpr int NT = 4 * DU;  // dV^T then dK^T MFMAs: index = (which, kc, u)
-    auto tnext = [&](int i) {
-      const int which = i / (2 * DU), kc = (i / DU) % 2, u = i % DU;
-      const lds_bf16* base = which == 0 ? ot : qt;
-      const bf16x4 lo = lds_read_tr4(base + toff[0][u] + 16 * kc * D);
-      const bf16x4 h4 = lds_read_tr4(base + toff[1][u] + 16 * kc * D);
-      return bf16x8{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
+  // ---- one tile: t in stage S, t+1 in stage S+1.  The body after the last
+  // tile also computes S, dP and P of a tile t+1 = nit, from whatever its
+  // stage holds; the loop ends before anything reads them.
+  auto body = [&](int t, auto s_t, auto mask_next_t, auto first_t) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_t)::value;
+    constexpr bool FIRST = decltype(first_t)::value;  // the first tile defines dK^T, dV^T
+    using S1 = Stage<S + 1>;
+    using S2 = Stage<S + 2>;
+    constexpr int NOPS = 4 * NP;
+    const bf16* qt = qst(s_t);
+    const bf16* ot = ost(s_t);
+    const bf16* qn = qst(S1{});
+    const bf16* on = ost(S1{});
+    const float* dt = dst(s_t);
+    const float* ln = lst(S1{});
+    __syncthreads();  // tile t+1 resident; every wave is done with tile t-1
+
+    // A operand of MFMA i of this body; i >= NOPS: of the next body's first ones.
+    auto aread = [&](auto i_t) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int i = decltype(i_t)::value;
+      constexpr int ph = i / NP, j = i % NP;
+      if constexpr (i >= NOPS) return tr_read(on, (i - NOPS) / DU, (i - NOPS) % DU);
+      else if constexpr (ph == 0) return tr_read(ot, j / DU, j % DU);
+      else if constexpr (ph == 1) return row_read(qn, j / KC, j % KC);
+      else if constexpr (ph == 2) return tr_read(qt, j / DU, j % DU);
+      else return row_read(on, j / KC, j % KC);
     };
-    ra[0] = tnext(0);
-    ra[1] = tnext(1);
+    f32x16 sn[2], pn[2];
+    bf16x8 dsb[4], pbn[4];
+    uint32_t zn = 0;
+    const int lo = mask_lo(t + 1);
+    // elementwise work: dS pairs during phases 0-1, P pairs during phases 2-3,
+    // 8 pairs per phase; the per-row values are read one group ahead
+    f32x4 dv4[8], lv4[8];
+    dv4[0] = rows4(dt, 0);
+    lv4[0] = rows4(ln, 0);
+    auto valu = [&](auto i_t) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_t)::value;
+      constexpr int ph = i / NP, j = i % NP;
+      constexpr int b0 = ((ph & 1) * NP + j) * 8 / NP, b1 = ((ph & 1) * NP + j + 1) * 8 / NP;
+      static_for<b1 - b0>([&](auto x_t) __attribute__((always_inline)) {
+        constexpr int b = b0 + decltype(x_t)::value, grp = b >> 1;
+        if constexpr (ph <= 1) {
+          if constexpr ((b & 1) == 0 && grp + 1 < 8) dv4[grp + 1] = rows4(dt, grp + 1);
+          ds_pair(dsb, 2 * b, dv4[grp]);
+        } else {
+          if constexpr ((b & 1) == 0 && grp + 1 < 8) lv4[grp + 1] = rows4(ln, grp + 1);
+          exp_pair(t + 1, sn, pbn, zn, 2 * b, lv4[grp], lo, mask_next_t);
+        }
+      });
+    };
     __builtin_amdgcn_sched_barrier(0);
-    // P~ and dS groups 0, 1 form chunk 0, used from MFMA 0.
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      if (i == 0) {
-        ds_elems(0);
-        ds_elems(1);
-      }
-      if (i + 2 < NT) ra[(i + 2) % 3] = tnext(i + 2);
-      const int which = i / (2 * DU), kc = (i / DU) % 2, u = i % DU;
-      if (which == 0) {
-        dvacc[u] = mfma32(ra[i % 3], pb[kc], dvacc[u]);
+    static_for<NOPS>([&](auto i_t) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_t)::value;
+      constexpr int pre = i + PD;
+      ring[pre % RG] = aread(std::integral_constant<int, pre>{});
+      // copies of tile t+2, one piece every other MFMA (a burst of them
+      // stalls the wave on the full memory queue)
+      if constexpr (i % 2 == 0 && i / 2 < NPIECE)
+        issue_piece(t + 2, S2{}, std::integral_constant<int, i / 2>{});
+      constexpr int ph = i / NP, j = i % NP;
+      const bf16x8& a = ring[i % RG];
+      if constexpr (ph == 0) {
+        if constexpr (FIRST && j / DU == 0)
+          mfma32_acc_first(dvacc[j % DU], a, spb[j / DU]);
+        else
+          mfma32_acc(dvacc[j % DU], a, spb[j / DU]);
+      } else if constexpr (ph == 1) {
+        sn[j / KC] = mfma32(a, kreg[j % KC], j % KC == 0 ? zero : sn[j / KC]);
+      } else if constexpr (ph == 2) {
+        if constexpr (FIRST && j / DU == 0)
+          mfma32_acc_first(dkacc[j % DU], a, dsb[j / DU]);
+        else
+          mfma32_acc(dkacc[j % DU], a, dsb[j / DU]);
       } else {
-        dkacc[u] = mfma32(ra[i % 3], dsb[kc], dkacc[u]);
+        pn[j / KC] = mfma32(a, vreg[j % KC], j % KC == 0 ? zero : pn[j / KC]);
       }
-      // groups 2, 3 (chunk 1) are first used by MFMA DU
-      if (i == 1) ds_elems(2);
-      if (i == DU - 1) ds_elems(3);
+      // the operands of the AccVGPR-form MFMAs of ops i-1 .. i-3 stay live
+      // until here: the MFMAs of two later ops (whole groups before this one)
+      // have issued since op i-3's
+      static_for<3>([&](auto d_t) __attribute__((always_inline)) {
+        constexpr int k = i - 1 - decltype(d_t)::value, kph = k / NP, kj = k % NP;
+        if constexpr (k >= 0 && (kph == 0 || kph == 2)) {
+          keep(ring[k % RG]);
+          keep(kph == 0 ? spb[kj / DU] : dsb[kj / DU]);
+        }
+      });
+      valu(i_t);
       __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      sp[a] = sn[a];
+      sdp[a] = pn[a];
     }
-    wait_vmem();  // next tile landed (this wave's share) before the next barrier
+#pragma unroll
+    for (int c = 0; c < 4; ++c) spb[c] = pbn[c];
+    zb = zn;
+    wait_vmem();  // tile t+2 landed (this wave's share) before the next barrier
   };
 
-  issue_tile(it0, P0{});
-  wait_vmem();
-  // Masked tiles come first; their count is even unless they run to the end.
-  int it = it0;
-  for (; it + 1 < it_free; it += 2) {
-    iter(it, P0{}, T_{});
-    iter(it + 1, P1{}, T_{});
+  // With a causal mask the block's diagonal spans its first two tiles: the
+  // prologue masks the first, the first body the second.
+  using CausalT = std::integral_constant<bool, CAUSAL>;
+  body(it0, Stage<0>{}, CausalT{}, T_{});
+  for (int t = it0 + 1;; t += 3) {
+    if (t >= nit) break;
+    body(t, Stage<1>{}, F_{}, F_{});
+    if (t + 1 >= nit) break;
+    body(t + 1, Stage<2>{}, F_{}, F_{});
+    if (t + 2 >= nit) break;
+    body(t + 2, Stage<0>{}, F_{}, F_{});
   }
-  if (it < it_free) {
-    iter(it, P0{}, T_{});
-    ++it;
-  }
-  for (; it + 1 < nit; it += 2) {
-    iter(it, P0{}, F_{});
-    iter(it + 1, P1{}, F_{});
-  }
-  if (it < nit) iter(it, P0{}, F_{});
-
-  // Add the row-half-1 partials into the row-half-0 waves through LDS (the
-  // K/V block buffer is free now), dK^T then dV^T: register r of tile u of
-  // lane l at (u*16 + r)*64 + l of the key group's slot.
-  float* const xs = (float*)skv;
-  static_assert(4 * D / 32 * 16 * 64 * 4 <= 2 * KTILE * 2, "exchange must fit the K/V buffer");
-  float* const mine = xs + kg * (DU * 16 * 64);
-  auto exchange = [&](f32x16 (&acc)[DU]) {
-    __syncthreads();
-    if (rh == 1) {
-#pragma unroll
-      for (int u = 0; u < DU; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mine[(u * 16 + r) * 64 + lane] = acc[u][r];
-    }
-    __syncthreads();
-    if (rh == 0) {
-#pragma unroll
-      for (int u = 0; u < DU; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[u][r] += mine[(u * 16 + r) * 64 + lane];
-    }
-  };
-  exchange(dkacc);
-  exchange(dvacc);
-  store_dkdv();
+  acc_settle();
+  store_dkdv(key >= L);
 }
 
 // ----------------------------------------------------------------------------

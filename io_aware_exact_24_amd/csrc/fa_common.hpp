@@ -7,6 +7,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef __bf16 bf16;
@@ -26,6 +29,26 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+// acc += A B with the accumulator pinned to AccVGPRs, for long-lived
+// accumulators that only MFMAs touch (the other MFMAs and the VALU keep the
+// ordinary VGPRs).  Dependent issues on the same accumulator need no wait
+// states; a VALU read of acc must follow acc_settle().
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// acc = A B (the first product into an accumulator: no prior value, so the
+// compiler has nothing to initialise or copy right before the MFMA reads it).
+__device__ __forceinline__ void mfma32_acc_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+}
+// The compiler does not know when an inline-asm MFMA has finished reading its
+// A/B registers; keep(x) after two later MFMA issues marks x as still in use
+// up to that point, so nothing overwrites it while the MFMA may read it.
+__device__ __forceinline__ void keep(const bf16x8& x) { asm volatile("" ::"v"(x)); }
+// Wait states covering the latency of the last mfma32_acc before its
+// accumulator is read.
+__device__ __forceinline__ void acc_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
 
 // LDS transposing read of four 16-bit elements.  Within each group of 16 lanes,
 // lane t receives element (t % 4) of the 8-byte load issued by lane 4*e + t/4 as
@@ -76,6 +99,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // computed at this point of the program, which keeps a reduction step inside
 // the MFMA group it was written in instead of being sunk past the loop.
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
 
 // m = max(m, a, b) as one v_max3_f32, placed where it is written (the scores
 // are never NaN, so the operand canonicalisation fmaxf would add is not needed).
@@ -162,6 +186,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, in order: every index
+// is a compile-time constant inside f.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace fa
