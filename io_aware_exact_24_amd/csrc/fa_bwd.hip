@@ -562,23 +562,31 @@ void bwd_dq_kernel(BwdParams p) {
 
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, (uint32_t)N * D * 2);
-  uint32_t ld_off[C::LOADS];
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int pch = (i * NW + wave) * 64 + lane;
-    const int r = pch / C::CHUNKS, pc = pch % C::CHUNKS;
-    ld_off[i] = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
+  // Byte offset of this lane's i-th 16-byte copy within a tile: chunk slot
+  // (i * NW + wave) * 64 + lane, i.e. row (i * NW + wave) * 64 / CHUNKS +
+  // lane / CHUNKS, chunk lane % CHUNKS.  The swizzle depends on the row mod 16,
+  // which does not change with i, so copy i is copy 0 moved by i * NW * 64
+  // chunks.
+  static_assert((NW * 64 / C::CHUNKS) % 16 == 0, "copy rows must keep their swizzle");
+  uint32_t ld_off0;
+  {
+    const int r = wave * 64 / C::CHUNKS + lane / C::CHUNKS, pc = lane % C::CHUNKS;
+    ld_off0 = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
   }
-  auto issue = [&](int jt, auto par_t) {
+  auto ld_off = [&](int i) { return ld_off0 + (uint32_t)(i * NW * 64 * 16); };
+  // Copy piece x of tile jt (x < LOADS: K, else V) into stage S.
+  auto issue_piece = [&](int jt, auto par_t, int x) {
     constexpr int S = decltype(par_t)::value;
-    bf16* kd = S ? sk1 : sk0;
-    bf16* vd = S ? sv1 : sv0;
     const uint32_t base = (uint32_t)jt * (BN * D * 2);
+    const int i = x % C::LOADS;
+    if (x < C::LOADS)
+      lds_dma16(krs, (S ? sk1 : sk0) + (i * NW + wave) * 512, ld_off(i) + base);
+    else
+      lds_dma16(vrs, (S ? sv1 : sv0) + (i * NW + wave) * 512, ld_off(i) + base);
+  };
+  auto issue = [&](int jt, auto par_t) {
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      lds_dma16(krs, kd + (i * NW + wave) * 512, ld_off[i] + base);
-      lds_dma16(vrs, vd + (i * NW + wave) * 512, ld_off[i] + base);
-    }
+    for (int x = 0; x < 2 * C::LOADS; ++x) issue_piece(jt, par_t, x);
   };
   // Row reads of K and V tiles (A operands of S^T and dP^T): row 32t + li,
   // logical chunk 2c + hh.  Transposing reads of the K tile (A operand of
@@ -612,7 +620,6 @@ void bwd_dq_kernel(BwdParams p) {
     const bf16* ks = S ? sk1 : sk0;
     const bf16* vs = S ? sv1 : sv0;
     __syncthreads();  // tile j resident; every wave is done with tile j-1
-    if (j + 1 < nkb) issue(j + 1, std::integral_constant<int, S ^ 1>{});
 
     // ---- S^T = K Q^T and dP^T = V dO^T: key tile t (32 keys), k-step c.
     f32x16 sacc[2], pacc[2];
@@ -651,6 +658,11 @@ void bwd_dq_kernel(BwdParams p) {
     };
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
+      // copies of tile j+1, one every other MFMA (a burst of them stalls the
+      // wave on the full memory queue); a tile past the end reads as zero
+      // into a stage nothing reads again
+      if (i % 2 == 0 && i / 2 < 2 * C::LOADS)
+        issue_piece(j + 1, std::integral_constant<int, S ^ 1>{}, i / 2);
       if (i + 2 < NS) ring[(i + 2) % 3] = sread(i + 2);
       const int m = i / KC, c = i % KC;
       f32x16& acc = m < 2 ? sacc[m & 1] : pacc[m & 1];

@@ -118,24 +118,31 @@ void fwd_bf16_kernel(FwdParams p) {
     }
   }
 
-  // Per-lane byte offsets of this thread's 16-byte copies within a tile.
-  uint32_t ld_off[C::LOADS];
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int pch = (i * NW + wave) * 64 + lane;  // physical chunk slot written by this lane
-    const int r = pch / C::CHUNKS, pc = pch % C::CHUNKS;
-    ld_off[i] = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
+  // Byte offset of this lane's i-th 16-byte copy within a tile: chunk slot
+  // (i * NW + wave) * 64 + lane, i.e. row (i * NW + wave) * 64 / CHUNKS +
+  // lane / CHUNKS, chunk lane % CHUNKS.  The swizzle depends on the row mod 16,
+  // which does not change with i, so copy i is copy 0 moved by i * NW * 64
+  // chunks.
+  static_assert((NW * 64 / C::CHUNKS) % 16 == 0, "copy rows must keep their swizzle");
+  uint32_t ld_off0;
+  {
+    const int r = wave * 64 / C::CHUNKS + lane / C::CHUNKS, pc = lane % C::CHUNKS;
+    ld_off0 = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
   }
+  auto ld_off = [&](int i) { return ld_off0 + (uint32_t)(i * NW * 64 * 16); };
+  auto issue_k_piece = [&](int jt, int stage, int i) {
+    lds_dma16(krs, kbuf(stage) + (i * NW + wave) * 512, ld_off(i) + (uint32_t)jt * (BN * D * 2));
+  };
+  auto issue_v_piece = [&](int jt, int stage, int i) {
+    lds_dma16(vrs, vbuf(stage) + (i * NW + wave) * 512, ld_off(i) + (uint32_t)jt * (BN * D * 2));
+  };
   auto issue_k = [&](int jt, int stage) {
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-      lds_dma16(krs, kbuf(stage) + (i * NW + wave) * 512, ld_off[i] + (uint32_t)jt * (BN * D * 2));
+    for (int i = 0; i < C::LOADS; ++i) issue_k_piece(jt, stage, i);
   };
   auto issue_v = [&](int jt, int stage) {
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-      lds_dma16(vrs, vbuf(stage) + (i * NW + wave) * 512,
-                ld_off[i] + (uint32_t)jt * (BN * D * 2));
+    for (int i = 0; i < C::LOADS; ++i) issue_v_piece(jt, stage, i);
   };
 
   // LDS element offsets of the MFMA operand reads (stage 0; stage 1 adds TILE).
@@ -248,8 +255,6 @@ void fwd_bf16_kernel(FwdParams p) {
     constexpr bool MASK_NEXT = decltype(mask_next_t)::value;
     constexpr int PAR = decltype(par_t)::value;  // j & 1
     __syncthreads();  // K_{j+1}, V_j resident; every wave is done with step j-1
-    if (j + 2 < nkb) issue_k(j + 2, PAR);
-    if (j + 1 < nkb) issue_v(j + 1, PAR ^ 1);
     rescale_if_needed(mx_cur);
     const float nm = mref == -INFINITY ? 0.0f : -mref;
 
@@ -267,6 +272,16 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int t = i / KC, c = i % KC;
+      // copies of K_{j+2} and V_{j+1}, one every other MFMA (a burst of them
+      // stalls the wave on the full memory queue); tiles past the end read as
+      // zero and land in stages nothing reads again
+      if (i % 2 == 0 && i / 2 < 2 * C::LOADS) {
+        const int x = i / 2;
+        if (x < C::LOADS)
+          issue_k_piece(j + 2, PAR, x);
+        else
+          issue_v_piece(j + 1, PAR ^ 1, x - C::LOADS);
+      }
       if constexpr (HAS_NEXT) {
         if (i + 2 < NA) ka[(i + 2) % 3] = kread(i + 2);
         const f32x16 zero = {};
