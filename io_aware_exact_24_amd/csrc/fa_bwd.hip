@@ -149,13 +149,21 @@ void bwd_dkdv_kernel(BwdParams p) {
   };
 
   const int N = p.N;
+  const int nb = p.num_blocks;
+  // With a causal mask key block b sees nit - 2b query tiles: a workgroup
+  // takes blocks w and nb-1-w in turn, so every workgroup does the same work.
+  const int per_head = CAUSAL ? (nb + 1) / 2 : nb;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = lid / p.num_blocks;
-  const int jb = lid - head * p.num_blocks;  // low key blocks see the most rows: run first
+  const int head = lid / per_head;
+  const int w = lid - head * per_head;
+  const int nitems = CAUSAL && w != nb - 1 - w ? 2 : 1;
   const int bi = head / p.H, hi = head - bi * p.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
+  for (int item = 0; item < nitems; ++item) {
+  if (item) __syncthreads();  // every wave is done with the first block's tiles
+  const int jb = item == 0 ? w : nb - 1 - w;
   const int kb = jb * BK;             // first key of the workgroup
   const int key = kb + 32 * wave + li;  // this lane's key (column of S)
 
@@ -197,7 +205,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         *(bf16x4*)(p.dv + head_off + (size_t)key * D + 4 * c + 4 * hh) = z;
       }
     }
-    return;
+    continue;
   }
 
   // K and V rows of this lane's key as B operands (k = head dimension).
@@ -490,6 +498,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
   acc_settle();
   store_dkdv(key >= L);
+  }  // item
 }
 
 // ----------------------------------------------------------------------------
@@ -520,13 +529,20 @@ void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 sv1[TILE];
 
   const int N = p.N;
+  const int nqb = p.num_blocks;
+  // Causal: a workgroup takes query blocks nqb-1-w and w in turn (equal work).
+  const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = lid / p.num_blocks;
-  const int qb = p.num_blocks - 1 - (lid - head * p.num_blocks);  // costliest blocks first
+  const int head = lid / per_head;
+  const int w = lid - head * per_head;
+  const int nitems = CAUSAL && w != nqb - 1 - w ? 2 : 1;
   const int bi = head / p.H, hi = head - bi * p.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
+  for (int item = 0; item < nitems; ++item) {
+  if (item) __syncthreads();  // every wave is done with the first block's tiles
+  const int qb = CAUSAL ? (item == 0 ? nqb - 1 - w : w) : w;
   const int q0 = qb * C::BM;
   const int qi = q0 + wave * 32 + li;  // this lane's query
 
@@ -732,6 +748,7 @@ void bwd_dq_kernel(BwdParams p) {
         *(bf16x4*)(qrow + 32 * u + 8 * g + 4 * hh) = ov;
       }
   }
+  }  // item
 }
 
 // D_i = sum_k dO_ik O_ik and LSE_i * log2(e) (+inf for an empty row, so that
@@ -766,14 +783,16 @@ template <int D, bool CAUSAL, bool DROPOUT>
 hipError_t launch_main(BwdParams p, int heads, int stages, hipStream_t s) {
   if (stages & kBwdKV) {
     p.num_blocks = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROPOUT>), dim3(heads * p.num_blocks),
+    const int per_head = CAUSAL ? (p.num_blocks + 1) / 2 : p.num_blocks;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROPOUT>), dim3(heads * per_head),
                        dim3(KvCfg<D>::THREADS), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kBwdQ) {
     p.num_blocks = (p.N + QCfg<D>::BM - 1) / QCfg<D>::BM;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROPOUT>), dim3(heads * p.num_blocks),
+    const int per_head = CAUSAL ? (p.num_blocks + 1) / 2 : p.num_blocks;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROPOUT>), dim3(heads * per_head),
                        dim3(QCfg<D>::THREADS), 0, s, p);
     return hipGetLastError();
   }

@@ -81,13 +81,22 @@ void fwd_bf16_kernel(FwdParams p) {
   auto vbuf = [&](int stage) -> bf16* { return stage ? sv1 : sv0; };
 
   const int N = p.N;
+  const int nqb = p.num_qblocks;
+  // With a causal mask query block b costs b + 1 key tiles: a workgroup takes
+  // blocks nqb-1-w and w in turn, so every workgroup does the same work (no
+  // stragglers at the end of the grid, half as many workgroup start-ups).
+  const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = lid / p.num_qblocks;                            // b * H + h
-  const int qb = p.num_qblocks - 1 - (lid - head * p.num_qblocks);  // costliest blocks first
+  const int head = lid / per_head;  // b * H + h
+  const int w = lid - head * per_head;
+  const int nitems = CAUSAL && w != nqb - 1 - w ? 2 : 1;
   const int bi = head / p.H, hi = head - bi * p.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
+  for (int item = 0; item < nitems; ++item) {
+  if (item) __syncthreads();  // every wave is done with the first block's tiles
+  const int qb = CAUSAL ? (item == 0 ? nqb - 1 - w : w) : w;
   const int q0 = qb * C::BM;
   const int qw = q0 + wave * 32;  // first query of this wave
   const int qi = qw + li;         // this lane's query
@@ -406,6 +415,7 @@ void fwd_bf16_kernel(FwdParams p) {
       p.lse[(size_t)head * N + qi] = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
     }
   }
+  }  // item
 }
 
 // fp32 path: one thread per query row, K/V tiles of 64 keys staged in LDS and
@@ -481,7 +491,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
 template <int D, bool CAUSAL, bool DROPOUT>
 hipError_t launch_bf16(const FwdParams& p, int heads, hipStream_t s) {
   using C = FwdCfg<D>;
-  const int grid = heads * p.num_qblocks;
+  const int grid = heads * (CAUSAL ? (p.num_qblocks + 1) / 2 : p.num_qblocks);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROPOUT>), dim3(grid), dim3(C::THREADS), 0, s, p);
   return hipGetLastError();
 }
