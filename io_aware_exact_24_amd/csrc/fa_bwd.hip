@@ -576,8 +576,11 @@ void bwd_dq_kernel(BwdParams p) {
   const float lrow = qi < N ? p.lse2[(size_t)head * N + qi] : INFINITY;
   const float drow = qi < N ? p.delta[(size_t)head * N + qi] : 0.0f;
 
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, (uint32_t)N * D * 2);
+  // The copies cover the tiles [0, nkb) only: copies past them (issued without
+  // a branch) read zeros without touching memory.
+  const uint32_t kv_bytes = (uint32_t)min(nkb * BN, N) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, kv_bytes);
   // Byte offset of this lane's i-th 16-byte copy within a tile: chunk slot
   // (i * NW + wave) * 64 + lane, i.e. row (i * NW + wave) * 64 / CHUNKS +
   // lane / CHUNKS, chunk lane % CHUNKS.  The swizzle depends on the row mod 16,

@@ -112,8 +112,11 @@ void fwd_bf16_kernel(FwdParams p) {
 
   const size_t head_off = (size_t)head * N * D;
   const bf16* __restrict__ qg = p.q + head_off;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, (uint32_t)N * D * 2);
+  // The copies cover the tiles [0, nkb) only: copies past them (issued without
+  // a branch) read zeros without touching memory.
+  const uint32_t kv_bytes = (uint32_t)min(nkb * BN, N) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, kv_bytes);
 
   // Q^T as the B operand of S^T = K Q^T: lane holds Q[qi][16c + 8hh .. +7].
   bf16x8 qreg[KC];
