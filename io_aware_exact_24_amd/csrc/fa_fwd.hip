@@ -271,6 +271,9 @@ void fwd_bf16_kernel(FwdParams p) {
     const float nm = mref == -INFINITY ? 0.0f : -mref;
 
     // ---- phase A
+    // Priority while this wave's exponentials are on the critical path: the
+    // other wave on the SIMD (in phase B, MFMA-bound) fills the gaps.
+    __builtin_amdgcn_s_setprio(3);
     const bf16* ks = kbuf(PAR ^ 1);
     auto kread = [&](int i) { return *(const bf16x8*)(ks + koff[i % KC] + (i / KC) * 32 * D); };
     bf16x8 pb[4];
@@ -339,6 +342,7 @@ void fwd_bf16_kernel(FwdParams p) {
     // chunk cc of pb covers keys 16cc .. 16cc+15; its k-slots match V^T below.
 
     // ---- phase B
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (HAS_NEXT && MASK_NEXT) apply_mask(j + 1, sn);
     const lds_bf16* vs = to_lds(vbuf(PAR));
     auto vread = [&](int idx) {
