@@ -5,8 +5,9 @@
 
 One step is the whole hot path on the causal decoder workload (B=4, H=32,
 N=4096, d=128, bf16, i.i.d. N(0,1) inputs drawn from a fixed seed): fa_fwd (O
-and LSE), then the backward as its three stages (fa_bwd_preprocess,
-fa_bwd_dkdv, fa_bwd_dq, exactly what fa_bwd enqueues) on the same stream,
+and LSE), then the backward as its two stages (fa_bwd_dq, which also computes
+the per-row terms D and LSE*log2e, then fa_bwd_dkdv: exactly what fa_bwd
+enqueues) on the same stream,
 inputs resident in device memory.  W untimed steps, then exactly K timed steps
 between device synchronisations; HIP events between the launches give each
 kernel's duration.  Prints one JSON line.
@@ -198,15 +199,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+    names = ("fwd", "bwd_dq", "bwd_dkdv")
 
     def step(ev=None):
         launches = (
             lambda: binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, 0.0, 0, stream),
-            lambda: binding.fa_bwd_preprocess(o, do, lse, ws, stream),
+            lambda: binding.fa_bwd_dq(q, k, v, o, do, lse, dq, w.scale, w.causal, None, 0.0, 0, ws,
+                                      stream),
             lambda: binding.fa_bwd_dkdv(q, k, v, do, dk, dv, w.scale, w.causal, None, 0.0, 0, ws,
                                         stream),
-            lambda: binding.fa_bwd_dq(q, k, v, do, dq, w.scale, w.causal, None, 0.0, 0, ws, stream),
         )
         for i, launch in enumerate(launches):
             if ev is not None:
@@ -231,7 +232,7 @@ def main():
     per = {n: sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps
            for i, n in enumerate(names)}
     avg_fwd = per["fwd"]
-    avg_bwd = per["bwd_pre"] + per["bwd_dkdv"] + per["bwd_dq"]
+    avg_bwd = per["bwd_dq"] + per["bwd_dkdv"]
     ms_per_step = wall * 1e3 / args.steps
     ff, fb = flops(B, H, N, d, w.causal)
     value = (ff + fb) / (ms_per_step * 1e-3) / 1e12

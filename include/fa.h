@@ -132,35 +132,41 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * The three stages fa_bwd runs, in order, on its stream.  They are exported
- * so that a caller can time them or overlap the two independent ones: once
- * fa_bwd_preprocess has completed, fa_bwd_dkdv and fa_bwd_dq only read the
- * inputs and the workspace and write disjoint outputs, so they may run on two
- * streams at once.  Arguments have the meaning and checks of fa_bwd; the
- * workspace must be the one fa_bwd_preprocess filled for the same o, dout
- * and lse, and must not change while the other stages run.
+ * The backward in stages.  fa_bwd enqueues fa_bwd_dq, then fa_bwd_dkdv, on its
+ * stream; they are exported so that a caller can time them, or compute dK/dV
+ * alone (fa_bwd_preprocess, then fa_bwd_dkdv).  Arguments have the meaning
+ * and checks of fa_bwd.
  *
- * fa_bwd_preprocess: D_i = sum_k dO_ik O_ik and LSE_i * log2(e) into the
- *   workspace (the backward's per-row terms).
+ * The workspace carries the backward's per-row terms, D_i = sum_k dO_ik O_ik
+ * and LSE_i * log2(e), from the stage that writes them (fa_bwd_dq or
+ * fa_bwd_preprocess) to fa_bwd_dkdv, which reads them: fa_bwd_dkdv must be
+ * ordered after one of the two (same stream, or an event), with the same o,
+ * dout and lse, and the workspace must not change while it runs.  The two
+ * writers compute D with different summation orders, so dK/dV after
+ * fa_bwd_preprocess can differ from fa_bwd's in the last bits.
+ *
+ * fa_bwd_preprocess: the per-row terms into the workspace.
+ * fa_bwd_dq: dQ, plus the per-row terms into the workspace.  Each 128-query
+ *   block is one workgroup that walks the key tiles, recomputing S = scale
+ *   Q K^T and dP = dO V^T from Q, K, V and the saved normaliser (ML Canon 48
+ *   FlashAttention, "backward without N x N"; Flash Attention hardware-aware
+ *   optimisation, section 2.2).
  * fa_bwd_dkdv: dK and dV.  Each 128-key block is one workgroup that walks the
- *   query tiles, recomputing S = scale Q K^T and dP = dO V^T from Q, K, V and
- *   the saved normaliser (ML Canon 48 FlashAttention, "backward without N x
- *   N"; Flash Attention hardware-aware optimisation, section 2.2).
- * fa_bwd_dq: dQ.  Each 128-query block is one workgroup that walks the key
- *   tiles, recomputing S and dP the same way.
+ *   query tiles, recomputing S and dP the same way.
  */
 fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
                             int B, int H, int N, int d, fa_dtype dtype,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq,
+                    int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                    const int32_t* key_lens, float dropout_p, uint64_t seed,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                       void* dk, void* dv, int B, int H, int N, int d, fa_dtype dtype,
                       float scale, int causal, const int32_t* key_lens, float dropout_p,
                       uint64_t seed, const void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
-fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
-                    int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
-                    const int32_t* key_lens, float dropout_p, uint64_t seed,
-                    const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* fa_status_string(fa_status s);

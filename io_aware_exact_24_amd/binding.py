@@ -56,7 +56,8 @@ def load_library():
     lib.fa_bwd_dkdv.restype = i
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64, vp, sz, vp]
     lib.fa_bwd_dq.restype = i
-    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64, vp, sz, vp]
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64, vp, sz,
+                              vp]
     _lib = lib
     return lib
 
@@ -175,7 +176,7 @@ def fa_bwd_preprocess(o, dout, lse, workspace, stream=None):
 
 def fa_bwd_dkdv(q, k, v, dout, dk, dv, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
                 workspace=None, stream=None):
-    """Enqueue the dK/dV stage (after fa_bwd_preprocess filled the workspace)."""
+    """Enqueue the dK/dV stage (after fa_bwd_dq or fa_bwd_preprocess filled the workspace)."""
     B, H, N, d, kl, ws_bytes = _bwd_common(
         q, (("k", k), ("v", v), ("dout", dout), ("dk", dk), ("dv", dv)), None, key_lens, workspace)
     st = load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dk), _ptr(dv), B, H,
@@ -186,15 +187,16 @@ def fa_bwd_dkdv(q, k, v, dout, dk, dv, scale, causal=False, key_lens=None, dropo
         raise FaError(st, "fa_bwd_dkdv")
 
 
-def fa_bwd_dq(q, k, v, dout, dq, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
+def fa_bwd_dq(q, k, v, o, dout, lse, dq, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
               workspace=None, stream=None):
-    """Enqueue the dQ stage (after fa_bwd_preprocess filled the workspace)."""
+    """Enqueue the dQ stage; it also writes the per-row terms (D, LSE*log2e)
+    into the workspace for fa_bwd_dkdv."""
     B, H, N, d, kl, ws_bytes = _bwd_common(
-        q, (("k", k), ("v", v), ("dout", dout), ("dq", dq)), None, key_lens, workspace)
-    st = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), B, H, N, d,
-                                  _dtype_code(q), float(scale), int(bool(causal)), _ptr(kl),
-                                  float(dropout_p), int(seed), _ptr(workspace), ws_bytes,
-                                  _stream(stream, q.device))
+        q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq)), lse, key_lens, workspace)
+    st = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                  _ptr(dq), B, H, N, d, _dtype_code(q), float(scale),
+                                  int(bool(causal)), _ptr(kl), float(dropout_p), int(seed),
+                                  _ptr(workspace), ws_bytes, _stream(stream, q.device))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_dq")
 

@@ -184,15 +184,15 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* d
                  causal, key_lens, dropout_p, seed, (void*)workspace, fa::kBwdKV, stream);
 }
 
-fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B,
-                    int H, int N, int d, fa_dtype dtype, float scale, int causal,
-                    const int32_t* key_lens, float dropout_p, uint64_t seed, const void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
-  const fa_status st = check_bwd({q, k, v, dout, dq}, key_lens, B, H, N, d, dtype, scale, dropout_p,
-                                 workspace, workspace_bytes);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, int B, int H, int N, int d, fa_dtype dtype,
+                    float scale, int causal, const int32_t* key_lens, float dropout_p,
+                    uint64_t seed, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const fa_status st = check_bwd({q, k, v, o, dout, lse, dq}, key_lens, B, H, N, d, dtype, scale,
+                                 dropout_p, workspace, workspace_bytes);
   if (st != FA_OK) return st;
-  return run_bwd(q, k, v, kUnused, dout, (const float*)kUnused, dq, nullptr, nullptr, B, H, N, d,
-                 scale, causal, key_lens, dropout_p, seed, (void*)workspace, fa::kBwdQ, stream);
+  return run_bwd(q, k, v, o, dout, lse, dq, nullptr, nullptr, B, H, N, d, scale, causal, key_lens,
+                 dropout_p, seed, workspace, fa::kBwdQ, stream);
 }
 
 }  // extern "C"

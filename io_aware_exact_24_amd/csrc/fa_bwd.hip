@@ -8,21 +8,26 @@
 //     dV = (P*Z)^T dO,   dP = dO V^T,   dS = P * (dP*Z - D),
 //     dK = scale * dS^T Q,   dQ = scale * dS K.
 //
-// Three kernels on one stream:
-//  1. bwd_pre:  D_i and LSE_i * log2(e) per row (fp32, in the workspace).
+// Two kernels on one stream, in this order:
+//  1. bwd_dq: one workgroup of 4 waves x 32 queries per query block; each
+//     wave keeps Q^T, dO^T and an fp32 dQ^T accumulator in registers and
+//     streams K/V tiles, recomputing S^T and dP^T (a lane per query, so LSE
+//     and D are per-lane scalars) and adding K^T dS^T.  Its prologue computes
+//     the per-row terms D_i = sum_k dO_ik O_ik and LSE_i * log2(e) from the
+//     dO row it already holds and one read of the O row, and writes them to
+//     the workspace.
 //  2. bwd_dkdv: one workgroup of 4 waves (one per SIMD) per 128-key block;
 //     each wave owns 32 keys and keeps their K and V rows (B operands) and the
 //     fp32 dK^T / dV^T accumulators (in AccVGPRs) in registers while the
-//     workgroup walks the 64-row query tiles that can see the block.  S and
+//     workgroup walks the 64-row query tiles that can see the block, reading
+//     D and LSE * log2(e) of each tile's rows from the workspace.  S and
 //     dP come out of the MFMA with a lane per key and 16 query rows per lane,
 //     which is the B-operand layout of the dV^T and dK^T products; their A
 //     operands dO^T and Q^T are transposing LDS reads of the row-major tiles.
 //     The products of tile t are skewed against those of tile t+1 so every
 //     group of MFMAs has independent elementwise work beside it.
-//  3. bwd_dq: one workgroup of 4 waves x 32 queries per query block; each
-//     wave keeps Q^T, dO^T and an fp32 dQ^T accumulator in registers and
-//     streams K/V tiles, recomputing S^T and dP^T (a lane per query, so LSE
-//     and D are per-lane scalars) and adding K^T dS^T.
+// bwd_pre computes the same per-row terms on its own, for a caller that wants
+// dK/dV without dQ.
 // Splitting dQ from dK/dV costs two extra products (S and dP are computed in
 // both kernels) but every gradient is accumulated in registers and written
 // once: no fp32 atomics (which on this part execute at the memory side, not
@@ -45,8 +50,10 @@ struct BwdParams {
   const bf16* k;
   const bf16* v;
   const bf16* dout;
-  const float* lse2;   // LSE * log2(e), +inf for rows without any allowed key
-  const float* delta;  // D
+  const bf16* o;       // forward output (read by the dQ kernel for D)
+  const float* lse;    // forward LSE (natural log; read by the dQ kernel)
+  float* lse2;         // LSE * log2(e), +inf for rows without any allowed key
+  float* delta;        // D
   bf16* dq;
   bf16* dk;
   bf16* dv;
@@ -572,9 +579,23 @@ void bwd_dq_kernel(BwdParams p) {
       }
     }
   }
-  // Rows past N or without any allowed key: +inf makes every P vanish.
-  const float lrow = qi < N ? p.lse2[(size_t)head * N + qi] : INFINITY;
-  const float drow = qi < N ? p.delta[(size_t)head * N + qi] : 0.0f;
+  // The per-row terms of this lane's query: D = sum_k dO_k O_k (each of the
+  // two lanes of a row holds half of the row's dO) and LSE * log2(e).  Rows
+  // past N or without any allowed key get +inf, which makes every P vanish.
+  // Both go to the workspace, where the dK/dV stage reads them.
+  float drow = 0.0f, lrow = INFINITY;
+  if (qi < N) {
+    const bf16* orow = p.o + head_off + (size_t)qi * D + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) drow = dot8(*(const bf16x8*)(orow + 16 * c), oreg[c], drow);
+    const float lv = p.lse[(size_t)head * N + qi];
+    lrow = lv == -INFINITY ? INFINITY : lv * kLog2e;
+  }
+  drow = pair_sum(drow);
+  if (hh == 0 && qi < N) {
+    p.delta[(size_t)head * N + qi] = drow;
+    p.lse2[(size_t)head * N + qi] = lrow;
+  }
 
   // The copies cover the tiles [0, nkb) only: copies past them (issued without
   // a branch) read zeros without touching memory.
@@ -784,19 +805,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
 
 template <int D, bool CAUSAL, bool DROPOUT>
 hipError_t launch_main(BwdParams p, int heads, int stages, hipStream_t s) {
-  if (stages & kBwdKV) {
-    p.num_blocks = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
-    const int per_head = CAUSAL ? (p.num_blocks + 1) / 2 : p.num_blocks;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROPOUT>), dim3(heads * per_head),
-                       dim3(KvCfg<D>::THREADS), 0, s, p);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // dQ first: it writes the per-row terms the dK/dV kernel reads.
   if (stages & kBwdQ) {
     p.num_blocks = (p.N + QCfg<D>::BM - 1) / QCfg<D>::BM;
     const int per_head = CAUSAL ? (p.num_blocks + 1) / 2 : p.num_blocks;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROPOUT>), dim3(heads * per_head),
                        dim3(QCfg<D>::THREADS), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kBwdKV) {
+    p.num_blocks = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
+    const int per_head = CAUSAL ? (p.num_blocks + 1) / 2 : p.num_blocks;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROPOUT>), dim3(heads * per_head),
+                       dim3(KvCfg<D>::THREADS), 0, s, p);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -829,6 +851,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
   p.k = (const bf16*)a.k;
   p.v = (const bf16*)a.v;
   p.dout = (const bf16*)a.dout;
+  p.o = (const bf16*)a.o;
+  p.lse = a.lse;
   p.lse2 = a.lse2;
   p.delta = a.delta;
   p.dq = (bf16*)a.dq;

@@ -13,6 +13,7 @@
 namespace fa {
 
 typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -94,6 +95,15 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// acc + sum_e a[e] * b[e] over eight bf16 pairs, as four v_dot2 (the bf16
+// products are exact in fp32; the sums are fp32).
+__device__ __forceinline__ float dot8(const bf16x8& a, const bf16x8& b, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; e += 2)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a[e], a[e + 1]}, bf16x2{b[e], b[e + 1]}, acc, false);
+  return acc;
+}
 
 // An empty instruction that claims to read and rewrite x: the value must be
 // computed at this point of the program, which keeps a reduction step inside

@@ -42,15 +42,18 @@ struct BwdArgs {
   float drop_scale;
   uint64_t seed;
   float* delta;   // workspace: fp32 [B, H, N], D_i = sum_k dO_ik O_ik
-  float* lse2;    // workspace: fp32 [B, H, N], LSE_i * log2(e)
+  float* lse2;    // workspace: fp32 [B, H, N], LSE_i * log2(e) (+inf for an empty row)
 };
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
-// Backward stages, selected by a bit mask: the per-row preprocessing (D and
-// LSE*log2e into the workspace), the dK/dV kernel and the dQ kernel.
-enum : int { kBwdPre = 1, kBwdKV = 2, kBwdQ = 4, kBwdAll = 7 };
+// Backward stages, selected by a bit mask and launched in this order: the
+// per-row preprocessing alone (D and LSE*log2e into the workspace), the dQ
+// kernel (which also computes those per-row terms and writes them to the
+// workspace), the dK/dV kernel (which reads them).  The full backward is
+// kBwdQ | kBwdKV.
+enum : int { kBwdPre = 1, kBwdKV = 2, kBwdQ = 4, kBwdAll = kBwdQ | kBwdKV };
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
 
 }  // namespace fa

@@ -117,7 +117,7 @@ def test_workspace_size_is_linear_in_n():
 
 def stage_calls(lib, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, scale=0.125, p=0.0, ws=P,
                 ws_bytes=None, null=None):
-    """The three backward stages with placeholder pointers; `null` names one
+    """The backward stages with placeholder pointers; `null` names one
     tensor argument to pass as NULL."""
     if ws_bytes is None:
         ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d, dtype)
@@ -130,8 +130,8 @@ def stage_calls(lib, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, scale=0.125, 
                                             ws_bytes, None),
         "dkdv": lib.fa_bwd_dkdv(t("q"), t("k"), t("v"), t("dout"), t("dk"), t("dv"), B, H, N, d,
                                 dtype, scale, 0, None, p, 0, ws, ws_bytes, None),
-        "dq": lib.fa_bwd_dq(t("q"), t("k"), t("v"), t("dout"), t("dq"), B, H, N, d, dtype, scale, 0,
-                            None, p, 0, ws, ws_bytes, None),
+        "dq": lib.fa_bwd_dq(t("q"), t("k"), t("v"), t("o"), t("dout"), t("lse"), t("dq"), B, H, N,
+                            d, dtype, scale, 0, None, p, 0, ws, ws_bytes, None),
     }
 
 
@@ -153,7 +153,7 @@ def test_backward_compute_stages_check_scale_and_dropout(lib, kw):
 @pytest.mark.parametrize("name,stage", [
     ("o", "preprocess"), ("dout", "preprocess"), ("lse", "preprocess"),
     ("q", "dkdv"), ("k", "dkdv"), ("v", "dkdv"), ("dout", "dkdv"), ("dk", "dkdv"), ("dv", "dkdv"),
-    ("q", "dq"), ("k", "dq"), ("v", "dq"), ("dout", "dq"), ("dq", "dq"),
+    ("q", "dq"), ("k", "dq"), ("v", "dq"), ("o", "dq"), ("dout", "dq"), ("lse", "dq"), ("dq", "dq"),
 ])
 def test_backward_stages_reject_null(lib, name, stage):
     assert stage_calls(lib, null=name)[stage] == INVALID
