@@ -359,7 +359,10 @@ void bwd_dkdv_kernel(BwdParams p) {
   // tile it0; the first operands of its body.
   issue_tile(it0, Stage<0>{});
   issue_tile(it0 + 1, Stage<1>{});
-  wait_vmem();
+  // Loads complete in issue order: once at most tile it0+1's pieces are
+  // outstanding, this wave's K/V rows and its share of tile it0 have landed.
+  // Tile it0+1 is awaited after the prologue's products.
+  wait_vmem_le<NPIECE>();
   __syncthreads();
   {
     const bf16* q = qst(Stage<0>{});
@@ -388,6 +391,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int i = 0; i < PD; ++i) ring[i] = tr_read(o, i / DU, i % DU);
+    wait_vmem();  // this wave's share of tile it0+1, before the first body's barrier
   }
 
   // ---- one tile: t in stage S, t+1 in stage S+1.  The body after the last

@@ -239,12 +239,20 @@ void fwd_bf16_kernel(FwdParams p) {
   if (nkb > 0) {
     issue_k(0, 0);
     issue_v(0, 0);
-    if (nkb > 1) issue_k(1, 1);
-    wait_vmem();
+    // Loads complete in issue order: with at most V_0's (and K_1's) pieces
+    // outstanding, Q and this wave's share of K_0 have landed.  V_0 and K_1
+    // arrive while the first scores are computed.
+    if (nkb > 1) {
+      issue_k(1, 1);
+      wait_vmem_le<2 * C::LOADS>();
+    } else {
+      wait_vmem_le<C::LOADS>();
+    }
     __syncthreads();
     qk(0, sa);
     if (nfree == 0) apply_mask(0, sa);
     mx_cur = tile_max(sa);
+    wait_vmem();  // this wave's share of V_0 and K_1, before the first step's barrier
   }
 
   // One pipeline step for tile j (scores in scur, row max mx_cur).
