@@ -40,10 +40,16 @@ def flops(B, H, N, d, causal):
     return f, 2.5 * f
 
 
-def source_digest():
+KERNEL_SOURCES = {"fwd_bf16_kernel": "fa_fwd.hip", "bwd_dkdv_kernel": "fa_bwd.hip",
+                  "bwd_dq_kernel": "fa_bwd.hip", "bwd_pre_kernel": "fa_bwd.hip"}
+
+
+def source_digest(kernel):
+    """Digest of the source file that defines `kernel` and of the headers every
+    kernel includes: it changes whenever that kernel's code can have changed."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "io_aware_exact_24_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in (KERNEL_SOURCES[kernel], "fa_common.hpp", "fa_internal.hpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -51,17 +57,17 @@ def source_digest():
 
 def stored_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary
-    profiles/traffic_decoder_causal.md, or None when the kernel sources changed
-    since the counters were taken (the summary records a digest of csrc/)."""
+    profiles/traffic_decoder_causal.md, or None when that kernel's sources
+    changed since the counters were taken (each row records a digest)."""
     path = os.path.join(ROOT, "profiles", "traffic_decoder_causal.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"source digest: `([0-9a-f]+)`", text)
-    if not m or m.group(1) != source_digest():
+    m = re.search(r"^\| `" + re.escape(kernel) + r"` \| `([0-9a-f]+)` \|[^|]*\|[^|]*\| ([0-9.e+]+) \|",
+                  text, re.M)
+    if not m or m.group(1) != source_digest(kernel):
         return None
-    m = re.search(r"^\| `" + re.escape(kernel) + r"` \|[^|]*\|[^|]*\| ([0-9.e+]+) \|", text, re.M)
-    return float(m.group(1)) if m else None
+    return float(m.group(2))
 
 
 def cpu_baseline(w, heads=CPU_SAMPLE_HEADS):
@@ -122,7 +128,7 @@ def summarize_traffic(fetch_dir, write_dir, out_path):
     rows = []
     for k in sorted(fetch):
         m = re.search(r"(\w+_kernel)", k)
-        if not m or "fa::" not in k or k not in write:
+        if not m or "fa::" not in k or k not in write or m.group(1) not in KERNEL_SOURCES:
             continue
         fk = sum(fetch[k]) / len(fetch[k]) * f_scale * 1024
         wk = sum(write[k]) / len(write[k]) * w_scale * 1024
@@ -143,13 +149,15 @@ def summarize_traffic(fetch_dir, write_dir, out_path):
         f"Calibration on the plain 256 MiB copy: FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f} "
         "give true bytes.",
         "",
-        f"source digest: `{source_digest()}`",
+        "The digest column identifies the kernel's sources the counters were taken on "
+        "(bench.py reports the bytes only while they still match).",
         "",
-        "| kernel | read (MiB) | written (MiB) | total bytes per launch |",
-        "|---|---|---|---|",
+        "| kernel | source digest | read (MiB) | written (MiB) | total bytes per launch |",
+        "|---|---|---|---|---|",
     ]
     for name, fk, wk in rows:
-        lines.append(f"| `{name}` | {fk / 2**20:.1f} | {wk / 2**20:.1f} | {fk + wk:.4e} |")
+        lines.append(f"| `{name}` | `{source_digest(name)}` | {fk / 2**20:.1f} | {wk / 2**20:.1f} | "
+                     f"{fk + wk:.4e} |")
     open(out_path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
