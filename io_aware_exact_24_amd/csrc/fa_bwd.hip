@@ -59,6 +59,7 @@ struct BwdParams {
   bf16* dv;
   const int32_t* key_lens;
   int H, N, num_blocks;
+  int units;  // dK/dV work units (blocks, or causal pairs of blocks) over all heads
   float scale, scale_log2;
   uint32_t drop_threshold;
   float drop_scale;
@@ -138,6 +139,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float sd0[BQ];
   __shared__ __attribute__((aligned(256))) float sd1[BQ];
   __shared__ __attribute__((aligned(256))) float sd2[BQ];
+  // K rows of the workgroup's key block (two 64-row tiles), copied in at the
+  // start of each block; its V rows go to stage 2 until the first body.
+  __shared__ __attribute__((aligned(1024))) bf16 skv[2 * TILE];
   auto qst = [&](auto s) __attribute__((always_inline)) -> bf16* {
     constexpr int S = decltype(s)::value;
     return S == 0 ? sq0 : S == 1 ? sq1 : sq2;
@@ -157,20 +161,57 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   const int N = p.N;
   const int nb = p.num_blocks;
-  // With a causal mask key block b sees nit - 2b query tiles: a workgroup
-  // takes blocks w and nb-1-w in turn, so every workgroup does the same work.
+  // Work units: with a causal mask key block b sees nit - 2b query tiles, so a
+  // unit is the pair of blocks w and nb-1-w (every unit the same work);
+  // without one, a unit is one block.  The grid is persistent (one workgroup
+  // per CU): each XCD takes a contiguous range of units (whole heads, whose
+  // Q/dO tiles then stay in that XCD's L2), dealt round-robin to its
+  // workgroups, and a workgroup walks its blocks as one chain, fetching the
+  // next block's K and V rows while it works on the current one.
   const int per_head = CAUSAL ? (nb + 1) / 2 : nb;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = lid / per_head;
-  const int w = lid - head * per_head;
-  const int nitems = CAUSAL && w != nb - 1 - w ? 2 : 1;
-  const int bi = head / p.H, hi = head - bi * p.H;
+  const int G = gridDim.x;
+  int u, ustep, uend;
+  if ((G & 7) == 0 && (p.units & 7) == 0) {
+    const int x = blockIdx.x & 7, per_x = p.units >> 3;
+    u = x * per_x + (blockIdx.x >> 3);
+    ustep = G >> 3;
+    uend = (x + 1) * per_x;
+  } else {
+    u = blockIdx.x;
+    ustep = G;
+    uend = p.units;
+  }
+  int sub = 0;  // which block of the unit
+  auto block_of = [&](int uu, int ss, int& head_, int& jb_) {
+    head_ = uu / per_head;
+    const int w = uu - head_ * per_head;
+    jb_ = ss == 0 ? w : nb - 1 - w;
+  };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
-  for (int item = 0; item < nitems; ++item) {
-  if (item) __syncthreads();  // every wave is done with the first block's tiles
-  const int jb = item == 0 ? w : nb - 1 - w;
+  // The next block's K rows (this lane's key) land here and its V rows in skv
+  // during the current block's first tile.
+  bf16x8 knext[KC];
+  bool prefetched = false, started = false;
+  while (u < uend) {
+  if (started) __syncthreads();  // every wave is done with the previous block's LDS
+  started = true;
+  int head, jb;
+  block_of(u, sub, head, jb);
+  {
+    const int w = u % per_head;
+    if (CAUSAL && sub == 0 && w != nb - 1 - w) {
+      sub = 1;
+    } else {
+      u += ustep;
+      sub = 0;
+    }
+  }
+  const bool has_next = u < uend;
+  int nhead = head, njb = jb;
+  if (has_next) block_of(u, sub, nhead, njb);
+  const int bi = head / p.H, hi = head - bi * p.H;
   const int kb = jb * BK;             // first key of the workgroup
   const int key = kb + 32 * wave + li;  // this lane's key (column of S)
 
@@ -184,26 +225,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   f32x16 dkacc[DU], dvacc[DU];
   // Keys past the key length take part in nothing: their gradients are zero.
   // Their lanes compute unmasked values (each lane's columns of S, dP, dV^T
-  // and dK^T depend on its own key only), which the store discards.
-  auto store_dkdv = [&](bool zero) __attribute__((always_inline)) {
-    if (key >= N) return;
-    bf16* dkrow = p.dk + head_off + (size_t)key * D;
-    bf16* dvrow = p.dv + head_off + (size_t)key * D;
-#pragma unroll
-    for (int u = 0; u < DU; ++u)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 kv, vv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kv[e] = zero ? (bf16)0.0f : (bf16)(dkacc[u][4 * g + e] * p.scale);
-          vv[e] = zero ? (bf16)0.0f : (bf16)dvacc[u][4 * g + e];
-        }
-        *(bf16x4*)(dkrow + 32 * u + 8 * g + 4 * hh) = kv;
-        *(bf16x4*)(dvrow + 32 * u + 8 * g + 4 * hh) = vv;
-      }
-  };
+  // and dK^T depend on its own key only), which the epilogue replaces by zeros.
   if (kb >= L) {  // every key of the block is padding
+    prefetched = false;  // the next block's rows are fetched at its start
     if (key < N) {
       const bf16x4 z = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
 #pragma unroll
@@ -215,21 +239,9 @@ void bwd_dkdv_kernel(BwdParams p) {
     continue;
   }
 
-  // K and V rows of this lane's key as B operands (k = head dimension).
+  // K and V rows of this lane's key as B operands (k = head dimension),
+  // read from LDS after the block's rows have been copied in.
   bf16x8 kreg[KC], vreg[KC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    if (key < N) {
-      kreg[c] = *(const bf16x8*)(p.k + head_off + (size_t)key * D + 16 * c + 8 * hh);
-      vreg[c] = *(const bf16x8*)(p.v + head_off + (size_t)key * D + 16 * c + 8 * hh);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kreg[c][e] = (bf16)0.0f;
-        vreg[c][e] = (bf16)0.0f;
-      }
-    }
-  }
 
   // Copies of Q and dO tiles with LSE*log2e and D (rows past N read as zero).
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q + head_off, (uint32_t)N * D * 2);
@@ -246,6 +258,26 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int r = wave * 64 / C::CHUNKS + lane / C::CHUNKS, pc = lane % C::CHUNKS;
     ld_off0 = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
   }
+  // K rows of block (head at hoff, first key kb_) straight into registers
+  // (this lane's key, rows past N read as zero), V rows into skv with the
+  // tiles' coalesced copy pattern: KC + 2 * LOADS memory operations.
+  constexpr int NFETCH = KC + 2 * C::LOADS;
+  auto fetch_kv = [&](size_t hoff, int kb_, bf16x8 (&kdst)[KC]) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + hoff, (uint32_t)N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + hoff, (uint32_t)N * D * 2);
+    const uint32_t krow = (uint32_t)(kb_ + 32 * wave + li) * (D * 2) + (uint32_t)(16 * hh);
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      kdst[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, krow + 32 * c, 0, 0));
+    const int kt0 = kb_ / BQ;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i)
+        lds_dma16(vrs, skv + h * TILE + (i * NW + wave) * 512,
+                  ld_off0 + (uint32_t)(kt0 + h) * (BQ * D * 2) + (uint32_t)(i * NW * 64 * 16));
+  };
+
   // Copy piece x of tile `it` into stage s: pieces 0 .. 2*LOADS-1 are this
   // wave's Q and dO chunks, piece 2*LOADS the per-row values (waves 0-1 copy
   // LSE*log2e, waves 2-3 copy D: duplicates of the same values, no branch).
@@ -357,13 +389,25 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   // ---- prologue: tiles it0 (stage 0) and it0 + 1 (stage 1); S, dP and P of
   // tile it0; the first operands of its body.
+  if (prefetched) {
+#pragma unroll
+    for (int c = 0; c < KC; ++c) kreg[c] = knext[c];
+  } else {
+    fetch_kv(head_off, kb, kreg);
+  }
   issue_tile(it0, Stage<0>{});
   issue_tile(it0 + 1, Stage<1>{});
   // Loads complete in issue order: once at most tile it0+1's pieces are
-  // outstanding, this wave's K/V rows and its share of tile it0 have landed.
-  // Tile it0+1 is awaited after the prologue's products.
+  // outstanding, the block's K/V rows and this wave's share of tile it0 have
+  // landed.  Tile it0+1 is awaited after the prologue's products.
   wait_vmem_le<NPIECE>();
   __syncthreads();
+  {
+    // V rows 32 * wave .. +31 of the block: 64-row tile wave / 2, half wave % 2.
+    const bf16* vt = skv + (wave >> 1) * TILE;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) vreg[c] = row_read(vt, wave & 1, c);
+  }
   {
     const bf16* q = qst(Stage<0>{});
     const bf16* o = ost(Stage<0>{});
@@ -492,7 +536,16 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) spb[c] = pbn[c];
     zb = zn;
-    wait_vmem();  // tile t+2 landed (this wave's share) before the next barrier
+    if (FIRST && !DROPOUT && has_next) {
+      // The next block's K/V rows, issued after this body's copies: they may
+      // stay in flight until the end of the next body (skv is free: every
+      // wave read its V rows before this body's barrier).  Not with dropout,
+      // whose keep-mask state leaves no registers for them.
+      fetch_kv((size_t)nhead * N * D, njb * BK, knext);
+      wait_vmem_le<NFETCH>();  // tile t+2 landed (this wave's share)
+    } else {
+      wait_vmem();  // tile t+2 landed (this wave's share) before the next barrier
+    }
   };
 
   // With a causal mask the block's diagonal spans its first two tiles: the
@@ -508,8 +561,22 @@ void bwd_dkdv_kernel(BwdParams p) {
     body(t + 2, Stage<0>{}, F_{}, F_{});
   }
   acc_settle();
-  store_dkdv(key >= L);
-  }  // item
+  // dK = scale * dK^T^T and dV through LDS (stages 0 and 1 are free once every
+  // wave is past the last tile), then whole rows to memory.  Keys past the key
+  // length get zeros; rows past N are not written.
+  __syncthreads();
+  {
+    const bool zero = key >= L;
+    bf16* kt = ((wave >> 1) ? so0 : sq0) + (wave & 1) * 32 * D;
+    bf16* vt = ((wave >> 1) ? so1 : sq1) + (wave & 1) * 32 * D;
+    acc_rows_to_lds<D>(kt, dkacc, p.scale, zero, li, hh);
+    acc_rows_to_lds<D>(vt, dvacc, 1.0f, zero, li, hh);
+    const int row0 = kb + 32 * wave;
+    lds_rows_to_global<D>(kt, p.dk + head_off + (size_t)row0 * D, N - row0, lane);
+    lds_rows_to_global<D>(vt, p.dv + head_off + (size_t)row0 * D, N - row0, lane);
+  }
+  prefetched = !DROPOUT && has_next;
+  }  // block
 }
 
 // ----------------------------------------------------------------------------
@@ -821,8 +888,17 @@ hipError_t launch_main(BwdParams p, int heads, int stages, hipStream_t s) {
   if (stages & kBwdKV) {
     p.num_blocks = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
     const int per_head = CAUSAL ? (p.num_blocks + 1) / 2 : p.num_blocks;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROPOUT>), dim3(heads * per_head),
-                       dim3(KvCfg<D>::THREADS), 0, s, p);
+    p.units = heads * per_head;
+    // Persistent grid: one workgroup per CU (each takes a whole CU's LDS and
+    // registers), at most one per unit.
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    const int grid = p.units < cus ? p.units : cus;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROPOUT>), dim3(grid), dim3(KvCfg<D>::THREADS), 0,
+                       s, p);
     return hipGetLastError();
   }
   return hipSuccess;

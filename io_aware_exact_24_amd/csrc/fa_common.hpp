@@ -157,6 +157,43 @@ __device__ __forceinline__ int swz(int r) {
   }
 }
 
+// Write a wave's 32 x D fp32 accumulator tile, held in the MFMA output layout
+// with one row per lane (lane li: row li; acc[u][r]: column 32u + 8(r/4) +
+// 4hh + r%4), as bf16 (acc * mul, or zeros) into a row-major 32 x D LDS tile
+// whose 16-byte chunks are XOR-swizzled by swz<D>(row).
+template <int D>
+__device__ __forceinline__ void acc_rows_to_lds(bf16* tile, const f32x16 (&acc)[D / 32], float mul,
+                                                bool zero, int li, int hh) {
+  // Opaque lane indices: the addresses are computed here, where they are
+  // used, rather than hoisted out of the caller's loop and kept live.
+  asm volatile("" : "+v"(li), "+v"(hh));
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = zero ? (bf16)0.0f : (bf16)(acc[u][4 * g + e] * mul);
+      *(bf16x4*)(tile + li * D + (((4 * u + g) ^ swz<D>(li)) * 8) + 4 * hh) = v;
+    }
+}
+
+// Copy rows [0, min(nrows, 32)) of such an LDS tile to global memory at dst
+// (row stride D elements), 16 bytes per lane: every store instruction writes
+// 64 / (D/8) whole rows, contiguous in memory.
+template <int D>
+__device__ __forceinline__ void lds_rows_to_global(const bf16* tile, bf16* dst, int nrows, int lane) {
+  constexpr int CH = D / 8, RPI = 64 / CH;
+  asm volatile("" : "+v"(lane));  // see acc_rows_to_lds
+  const int c = lane % CH;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CH;
+    const bf16x8 v = *(const bf16x8*)(tile + r * D + ((c ^ swz<D>(r)) * 8));
+    if (r < nrows) *(bf16x8*)(dst + (size_t)r * D + c * 8) = v;
+  }
+}
+
 // Remap a linear workgroup id so that consecutive logical ids run on the same
 // XCD.  The dispatcher deals workgroups round-robin to the 8 XCDs, so physical
 // id p lands on XCD p % 8; logical id (p % 8) * (G / 8) + p / 8 puts each XCD's
