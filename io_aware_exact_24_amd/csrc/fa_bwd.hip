@@ -831,17 +831,14 @@ void bwd_dq_kernel(BwdParams p) {
   }
   if (j < nkb) step(j, P0{}, T_{});
 
-  if (qi < N) {
-    bf16* qrow = p.dq + head_off + (size_t)qi * D;
-#pragma unroll
-    for (int u = 0; u < DU; ++u)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 ov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(qacc[u][4 * g + e] * p.scale);
-        *(bf16x4*)(qrow + 32 * u + 8 * g + 4 * hh) = ov;
-      }
+  // dQ = scale * dQ^T^T, transposed through the K stages (free once every
+  // wave is past the last tile) and written as whole rows.
+  __syncthreads();
+  {
+    const int qw = q0 + wave * 32;
+    bf16* qt = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
+    acc_rows_to_lds<D>(qt, qacc, p.scale, false, li, hh);
+    lds_rows_to_global<D>(qt, p.dq + head_off + (size_t)qw * D, N - qw, lane);
   }
   }  // item
 }

@@ -412,23 +412,19 @@ void fwd_bf16_kernel(FwdParams p) {
       step(j, F{}, F{}, P0{}, sa, sb);
   }
 
-  // Epilogue: O = O^T / l, LSE = (mref + log2 l) * ln 2.
+  // Epilogue: O = O^T / l, transposed through the K stages (free once every
+  // wave is past the last tile) and written as whole rows; LSE = (mref +
+  // log2 l) * ln 2.
   const float lt = pair_sum(l);
-  if (qi < N) {
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    bf16* orow = p.o + head_off + (size_t)qi * D;
-#pragma unroll
-    for (int u = 0; u < DU; ++u)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 ov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(oacc[u][4 * g + e] * inv);
-        *(bf16x4*)(orow + 32 * u + 8 * g + 4 * hh) = ov;
-      }
-    if (hh == 0) {
-      p.lse[(size_t)head * N + qi] = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
-    }
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  __syncthreads();
+  {
+    bf16* ot = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
+    acc_rows_to_lds<D>(ot, oacc, inv, false, li, hh);
+    lds_rows_to_global<D>(ot, p.o + head_off + (size_t)qw * D, N - qw, lane);
+  }
+  if (qi < N && hh == 0) {
+    p.lse[(size_t)head * N + qi] = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
   }
   }  // item
 }
