@@ -51,7 +51,8 @@ def f64(t):
 def max_abs(a, b):
     a, b = np.asarray(a), np.asarray(b)
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    d = np.where(both_inf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):  # -inf - -inf on empty rows, masked here
+        d = np.where(both_inf, 0.0, np.abs(a - b))
     return float(np.max(d)) if d.size else 0.0
 
 

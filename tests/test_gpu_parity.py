@@ -364,3 +364,47 @@ def test_backward_stages_equal_fa_bwd(causal, padded, p):
         a, b = a.double(), b.double()
         rel = ((a - b).norm() / b.norm()).item()
         assert rel <= 1e-3, (name, rel)
+
+
+# Shapes with more dK/dV work units (key blocks, or causal pairs of blocks)
+# than the GPU has CUs, so each persistent workgroup walks a chain of blocks and
+# fetches the next block's K/V rows during the current one: key padding with an
+# empty batch entry (fully padded blocks inside a chain), the XCD-split unit
+# order (units a multiple of 8) and the plain one (258 units), d = 64 and 128.
+CHAINS = [
+    # B, H, N, d, causal, key lengths (None: all N)
+    (4, 16, 1024, 128, False, [1024, 300, 777, 513]),
+    (4, 32, 1024, 128, True, [0, 1000, 1024, 511]),
+    (2, 32, 2048, 64, True, None),
+    (3, 43, 256, 64, False, [256, 100, 0]),
+]
+
+
+@pytest.mark.parametrize("case", CHAINS, ids=lambda c: "B{}H{}N{}d{}{}{}".format(
+    *c[:4], "-causal" if c[4] else "", "-pad" if c[5] else ""))
+def test_dkdv_block_chains(case):
+    B, H, N, d, causal, lens = case
+    inp = draw(B, H, N, d, torch.bfloat16, seed=CHAINS.index(case) + 500)
+    if lens is not None:
+        inp = Inputs(inp.q, inp.k, inp.v, inp.dout, torch.tensor(lens, dtype=torch.int32))
+    scale = float(np.float32(1 / np.sqrt(d)))
+    note(f"chain case {case}")
+    o, lse = gpu_forward(inp, scale, causal)
+    dq, dk, dv = gpu_backward(inp, o, lse, scale, causal)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    if lens is not None:
+        # keys past the length get exactly zero gradients (every head)
+        for b, L in enumerate(lens):
+            assert torch.count_nonzero(dk[b, :, L:]) == 0 and torch.count_nonzero(dv[b, :, L:]) == 0
+    # sampled heads against the oracle, one (b, h) at a time: first, last and
+    # a spread of heads in between (each batch entry at least once)
+    heads = sorted({(b, h) for b in range(B) for h in (0, H - 1)} | {(B // 2, H // 2)})
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        kl = None if lens is None else [lens[b]]
+        q, k, v, do = (t[sl] for t in (inp.q, inp.k, inp.v, inp.dout))
+        ro, rlse = attention_forward(q, k, v, scale, causal, kl)
+        check_fwd(o[sl], lse[sl], ro, rlse, what=f"{case} head {(b, h)}")
+        ref = attention_backward(q, k, v, do, scale, causal, kl)
+        check_bwd((dq[sl], dk[sl], dv[sl]), ref, what=f"{case} head {(b, h)}")
