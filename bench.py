@@ -162,6 +162,75 @@ def summarize_traffic(fetch_dir, write_dir, out_path):
     print("\n".join(lines))
 
 
+def unmasked_pairs(w, key_lens):
+    """Unmasked (query, key) pairs of a workload, the unit of its FLOP count:
+    N^2/2 per head with a causal mask (the survey's convention), N * L_b per
+    head with key lengths L_b, N^2 otherwise."""
+    if w.causal:
+        return w.B * w.H * w.N * w.N / 2
+    if key_lens is not None:
+        return w.H * w.N * float(sum(int(x) for x in key_lens))
+    return w.B * w.H * w.N * w.N
+
+
+def all_configs(steps, warmup):
+    """Time fa_fwd and fa_bwd on every workload (one JSON line each): inputs
+    resident on the GPU, HIP events around `steps` back-to-back calls on the
+    library's stream after `warmup` untimed ones.  A report, not the metric
+    line: forward FLOP = 4 d per unmasked pair, backward 2.5x the forward."""
+    import torch
+
+    from io_aware_exact_24_amd import binding
+    from io_aware_exact_24_amd.workloads import DROPOUT_SEED, WORKLOADS, draw_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    for n, w in sorted(WORKLOADS.items()):
+        inp = draw_workload(w)
+        q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+        kl = None if inp.key_lens is None else inp.key_lens.to(dev)
+        seed = DROPOUT_SEED if w.dropout_p > 0 else 0
+        B, H, N, d = w.B, w.H, w.N, w.d
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        ff = 4.0 * d * unmasked_pairs(w, inp.key_lens)
+        rec = {"workload": f"{w.name}: B={B} H={H} N={N} d={d} {w.dtype}"
+                           f"{' causal' if w.causal else ''}{' key-padding' if w.padded else ''}"
+                           f"{f' dropout {w.dropout_p}' if w.dropout_p else ''}",
+               "dtype": w.dtype}
+        t = timed(lambda: binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal, kl, w.dropout_p, seed,
+                                         stream))
+        rec["fwd"] = {"ms": round(t, 4), "tflops": round(ff / t / 1e9, 2),
+                      "frac_of_peak": round(ff / t / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        if w.backward:
+            do = inp.dout.to(dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+            ws = torch.empty(binding.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8,
+                             device=dev)
+            t = timed(lambda: binding.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.scale, w.causal, kl,
+                                             w.dropout_p, seed, ws, stream))
+            fb = 2.5 * ff
+            rec["bwd"] = {"ms": round(t, 4), "tflops": round(fb / t / 1e9, 2),
+                          "frac_of_peak": round(fb / t / 1e9 / PEAK_BF16_TFLOPS, 4)}
+            del do, dq, dk, dv, ws
+        print(json.dumps(rec), flush=True)
+        del q, k, v, o, lse, kl
+        torch.cuda.empty_cache()
+
+
 def main():
     if len(sys.argv) == 4 and sys.argv[1] == "--summarize-traffic":
         summarize_traffic(sys.argv[2], sys.argv[3],
@@ -172,6 +241,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="time forward and backward on every workload (one JSON line each) instead")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -180,6 +251,10 @@ def main():
               "component (heads and batch entries shard with no exchange); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.all_configs:
+        all_configs(args.steps, args.warmup)
+        return
 
     import torch
 
