@@ -97,12 +97,29 @@ struct KvCfg {
 template <int S>
 using Stage = std::integral_constant<int, S % 3>;
 
-// Keep decision of element (row, key) for dropout.
-__device__ __forceinline__ bool dropout_keep(const BwdParams& p, int row, int key, int hi, int bi) {
-  const u32x4 w = philox((uint32_t)key >> 2, (uint32_t)row, (uint32_t)hi, (uint32_t)bi, p.seed_lo,
-                         p.seed_hi);
-  const uint32_t word = (key & 3) == 0 ? w[0] : (key & 3) == 1 ? w[1] : (key & 3) == 2 ? w[2] : w[3];
-  return word >= p.drop_threshold;
+// Keep bits of rows row0 .. row0+3 at this lane's key (bit e: row row0 + e),
+// for a lane whose quad (lanes 4m .. 4m+3) holds the keys 4m' .. 4m'+3 of one
+// Philox counter group (key & 3 == lane & 3).  Lane q draws the counter of row
+// row0 + q, whose four words are the four keys' draws at that row, and the
+// quad transposes the 4 x 4 words with DPP quad permutes: one Philox block per
+// lane for four elements instead of one per element.
+__device__ __forceinline__ uint32_t quad_keep4(const BwdParams& p, int row0, int key, int hi,
+                                               int bi) {
+  const int q = threadIdx.x & 3;
+  const u32x4 w = philox((uint32_t)key >> 2, (uint32_t)(row0 + q), (uint32_t)hi, (uint32_t)bi,
+                         p.seed_lo, p.seed_hi);
+  uint32_t bits = 0;
+  static_for<4>([&](auto j_t) {
+    constexpr int j = decltype(j_t)::value;
+    // Lane q reads lane (q + j) & 3, which sends word (sender - j) & 3 = q of
+    // its row's counter: this lane's key at row row0 + ((q + j) & 3).
+    const int idx = (q - j) & 3;
+    const uint32_t send = idx == 0 ? w[0] : idx == 1 ? w[1] : idx == 2 ? w[2] : w[3];
+    constexpr int ctrl = (j & 3) | (((1 + j) & 3) << 2) | (((2 + j) & 3) << 4) | (((3 + j) & 3) << 6);
+    const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, ctrl, 0xF, 0xF, false);
+    bits |= (uint32_t)(got >= p.drop_threshold) << ((q + j) & 3);
+  });
+  return bits;
 }
 
 // One wave per SIMD, each owning 32 keys of the block: their K and V rows
@@ -365,8 +382,9 @@ void bwd_dkdv_kernel(BwdParams p) {
       s[a][r + x] = pv;
       float pt = pv;
       if constexpr (DROPOUT) {
-        const bool keep = dropout_keep(p, it * BQ + 32 * a + 8 * g + 4 * hh + e + x, key, hi, bi);
-        zn |= (uint32_t)keep << (k + x);
+        // the keep bits of the group's four rows, drawn with the first pair
+        if (e + x == 0) zn |= quad_keep4(p, it * BQ + 32 * a + 8 * g + 4 * hh, key, hi, bi) << k;
+        const bool keep = (zn >> (k + x)) & 1;
         pt = keep ? pv * p.drop_scale : 0.0f;
       }
       pb[2 * a + (g >> 1)][4 * (g & 1) + e + x] = (bf16)pt;
