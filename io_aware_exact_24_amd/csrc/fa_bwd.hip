@@ -653,38 +653,9 @@ void bwd_dq_kernel(BwdParams p) {
 
   const size_t head_off = (size_t)head * N * D;
   // Q^T and dO^T as B operands (k = head dimension): lane holds row qi,
-  // elements 16c + 8hh .. +7.
+  // elements 16c + 8hh .. +7, read from LDS after the block's rows have been
+  // copied in (below).
   bf16x8 qreg[KC], oreg[KC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    if (qi < N) {
-      qreg[c] = *(const bf16x8*)(p.q + head_off + (size_t)qi * D + 16 * c + 8 * hh);
-      oreg[c] = *(const bf16x8*)(p.dout + head_off + (size_t)qi * D + 16 * c + 8 * hh);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qreg[c][e] = (bf16)0.0f;
-        oreg[c][e] = (bf16)0.0f;
-      }
-    }
-  }
-  // The per-row terms of this lane's query: D = sum_k dO_k O_k (each of the
-  // two lanes of a row holds half of the row's dO) and LSE * log2(e).  Rows
-  // past N or without any allowed key get +inf, which makes every P vanish.
-  // Both go to the workspace, where the dK/dV stage reads them.
-  float drow = 0.0f, lrow = INFINITY;
-  if (qi < N) {
-    const bf16* orow = p.o + head_off + (size_t)qi * D + 8 * hh;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) drow = dot8(*(const bf16x8*)(orow + 16 * c), oreg[c], drow);
-    const float lv = p.lse[(size_t)head * N + qi];
-    lrow = lv == -INFINITY ? INFINITY : lv * kLog2e;
-  }
-  drow = pair_sum(drow);
-  if (hh == 0 && qi < N) {
-    p.delta[(size_t)head * N + qi] = drow;
-    p.lse2[(size_t)head * N + qi] = lrow;
-  }
 
   // The copies cover the tiles [0, nkb) only: copies past them (issued without
   // a branch) read zeros without touching memory.
@@ -724,6 +695,50 @@ void bwd_dq_kernel(BwdParams p) {
   int roff[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) roff[c] = li * D + (((2 * c + hh) ^ rsw) * 8);
+  {
+    // The block's Q rows go through the K stages and its dO rows through the
+    // V stages (two 64-row tiles each) with the tiles' coalesced copies (rows
+    // past N read as zero); every wave then reads its rows into registers.
+    // Loading them straight into registers, a lane per row, cost more than
+    // this whole round trip.  The stages are free again after the barrier.
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q + head_off, (uint32_t)N * D * 2);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.dout + head_off, (uint32_t)N * D * 2);
+    const uint32_t qt0 = (uint32_t)(q0 / BN) * (BN * D * 2);
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      lds_dma16(qrs, sk0 + (i * NW + wave) * 512, ld_off(i) + qt0);
+      lds_dma16(qrs, sk1 + (i * NW + wave) * 512, ld_off(i) + qt0 + (uint32_t)(BN * D * 2));
+      lds_dma16(ors, sv0 + (i * NW + wave) * 512, ld_off(i) + qt0);
+      lds_dma16(ors, sv1 + (i * NW + wave) * 512, ld_off(i) + qt0 + (uint32_t)(BN * D * 2));
+    }
+    wait_vmem();
+    __syncthreads();
+    const bf16* qt = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
+    const bf16* ot = ((wave >> 1) ? sv1 : sv0) + (wave & 1) * 32 * D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      qreg[c] = *(const bf16x8*)(qt + roff[c]);
+      oreg[c] = *(const bf16x8*)(ot + roff[c]);
+    }
+    __syncthreads();  // every wave has its rows before the first K/V tile lands there
+  }
+  // The per-row terms of this lane's query: D = sum_k dO_k O_k (each of the
+  // two lanes of a row holds half of the row's dO) and LSE * log2(e).  Rows
+  // past N or without any allowed key get +inf, which makes every P vanish.
+  // Both go to the workspace, where the dK/dV stage reads them.
+  float drow = 0.0f, lrow = INFINITY;
+  if (qi < N) {
+    const bf16* orow = p.o + head_off + (size_t)qi * D + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) drow = dot8(*(const bf16x8*)(orow + 16 * c), oreg[c], drow);
+    const float lv = p.lse[(size_t)head * N + qi];
+    lrow = lv == -INFINITY ? INFINITY : lv * kLog2e;
+  }
+  drow = pair_sum(drow);
+  if (hh == 0 && qi < N) {
+    p.delta[(size_t)head * N + qi] = drow;
+    p.lse2[(size_t)head * N + qi] = lrow;
+  }
   const int g16 = lane & 15;
   const int trow = 4 * hh + (g16 >> 2);
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
