@@ -139,11 +139,11 @@ def summarize_traffic(fetch_dir, write_dir, out_path):
         "Commands (from the repository root, one MI355X):",
         "",
         "```",
-        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch -o p -- "
-        "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
-        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write -o p -- "
-        "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
-        "python bench.py --summarize-traffic gpurun_out/pmc/fetch gpurun_out/pmc/write",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o p -- "
+        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o p -- "
+        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
+        f"python bench.py --summarize-traffic {fetch_dir} {write_dir}",
         "```",
         "",
         f"Calibration on the plain 256 MiB copy: FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f} "
@@ -164,7 +164,7 @@ def summarize_traffic(fetch_dir, write_dir, out_path):
 
 def unmasked_pairs(w, key_lens):
     """Unmasked (query, key) pairs of a workload, the unit of its FLOP count:
-    N^2/2 per head with a causal mask (the survey's convention), N * L_b per
+    N^2/2 per head with a causal mask (the N/2 diagonal pairs not counted), N * L_b per
     head with key lengths L_b, N^2 otherwise."""
     if w.causal:
         return w.B * w.H * w.N * w.N / 2
