@@ -1,0 +1,91 @@
+"""PyTorch autograd entry point over the C ABI (argument marshalling only).
+
+`flash_attention` runs fa_fwd in the forward of a torch.autograd.Function and
+fa_bwd in its backward, keeping only what the recompute backward needs: Q, K,
+V, O and the per-row log-sum-exp (no N x N matrix; ML Canon 48 FlashAttention,
+"backward without N x N").  `scaled_dot_product_attention` takes the argument
+names of torch.nn.functional.scaled_dot_product_attention, the drop-in call the
+same page shows, for the cases the library computes.
+
+The kernels take contiguous [B, H, N, d] tensors.  layout="bnhd" accepts
+[B, N, H, d] (the layout of a fused QKV projection) and returns O in it; the
+tensors are then transposed into contiguous copies on the way in (and dO, dQ,
+dK, dV on the way through the backward), which costs one extra pass over each.
+"""
+
+import torch
+
+from . import binding
+
+
+def _to_bhnd(t, layout):
+    if layout == "bhnd":
+        return t.contiguous()
+    if layout == "bnhd":
+        return t.transpose(1, 2).contiguous()
+    raise ValueError(f"layout must be 'bhnd' or 'bnhd', not {layout!r}")
+
+
+def _from_bhnd(t, layout):
+    return t if layout == "bhnd" else t.transpose(1, 2)
+
+
+class FlashAttentionFunction(torch.autograd.Function):
+    """O = softmax(mask(scale * Q K^T)) (with dropout) V on [B, H, N, d]."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale, causal, key_lens, dropout_p, seed):
+        o, lse = binding.forward(q, k, v, scale, causal, key_lens, dropout_p, seed)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.key_lens = key_lens
+        ctx.args = (scale, causal, dropout_p, seed)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        scale, causal, dropout_p, seed = ctx.args
+        dq, dk, dv = binding.backward(q, k, v, o, do.contiguous(), lse, scale, causal,
+                                      ctx.key_lens, dropout_p, seed)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def flash_attention(q, k, v, scale=None, causal=False, key_lens=None, dropout_p=0.0, seed=None,
+                    layout="bhnd"):
+    """Exact attention with autograd support.
+
+    q, k, v: bf16 CUDA tensors [B, H, N, d] (layout="bhnd") or [B, N, H, d]
+    (layout="bnhd"), d in {64, 128}; fp32 is accepted without autograd
+    (forward only).  scale defaults to 1/sqrt(d).  key_lens: int32 [B]
+    (device or host) masking keys j >= key_lens[b].  dropout_p > 0 draws a
+    Philox seed from torch's default CPU generator when seed is None; the same
+    seed is replayed in the backward.
+    """
+    d = q.shape[-1]
+    if scale is None:
+        scale = d ** -0.5
+    if seed is None:
+        seed = int(torch.randint(0, 2**62, (1,)).item()) if dropout_p > 0.0 else 0
+    if key_lens is not None:
+        key_lens = key_lens.to(device=q.device, dtype=torch.int32)
+    qb, kb, vb = (_to_bhnd(t, layout) for t in (q, k, v))
+    if torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v)):
+        o = FlashAttentionFunction.apply(qb, kb, vb, float(scale), bool(causal), key_lens,
+                                         float(dropout_p), int(seed))
+    else:
+        o, _ = binding.forward(qb, kb, vb, float(scale), bool(causal), key_lens, float(dropout_p),
+                               int(seed))
+    return _from_bhnd(o, layout)
+
+
+def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.0,
+                                 is_causal=False, scale=None):
+    """torch.nn.functional.scaled_dot_product_attention's arguments on [B, H, N, d].
+
+    attn_mask is not supported (use flash_attention's key_lens for key
+    padding); a causal mask is square and top-left, key j visible to query i
+    iff j <= i.
+    """
+    if attn_mask is not None:
+        raise NotImplementedError("attn_mask is not supported; use flash_attention(key_lens=...)")
+    return flash_attention(query, key, value, scale=scale, causal=is_causal, dropout_p=dropout_p)
