@@ -10,17 +10,19 @@
 //
 // Two kernels on one stream, in this order:
 //  1. bwd_dq: one workgroup of 4 waves x 32 queries per query block; each
-//     wave keeps Q^T, dO^T and an fp32 dQ^T accumulator in registers and
-//     streams K/V tiles, recomputing S^T and dP^T (a lane per query, so LSE
-//     and D are per-lane scalars) and adding K^T dS^T.  Its prologue computes
-//     the per-row terms D_i = sum_k dO_ik O_ik and LSE_i * log2(e) from the
-//     dO row it already holds and one read of the O row, and writes them to
-//     the workspace.
-//  2. bwd_dkdv: one workgroup of 4 waves (one per SIMD) per 128-key block;
-//     each wave owns 32 keys and keeps their K and V rows (B operands) and the
-//     fp32 dK^T / dV^T accumulators (in AccVGPRs) in registers while the
-//     workgroup walks the 64-row query tiles that can see the block, reading
-//     D and LSE * log2(e) of each tile's rows from the workspace.  S and
+//     wave keeps Q^T, dO^T (brought in through LDS by coalesced copies) and
+//     an fp32 dQ^T accumulator in registers and streams K/V tiles,
+//     recomputing S^T and dP^T (a lane per query, so LSE and D are per-lane
+//     scalars) and adding K^T dS^T.  Its prologue computes the per-row terms
+//     D_i = sum_k dO_ik O_ik and LSE_i * log2(e) from the dO row it holds and
+//     one read of the O row, and writes them to the workspace.
+//  2. bwd_dkdv: persistent, one workgroup of 4 waves (one per SIMD) per CU,
+//     walking a chain of 128-key blocks; each wave owns 32 keys and keeps
+//     their K and V rows (B operands) and the fp32 dK^T / dV^T accumulators
+//     (in AccVGPRs) in registers while the workgroup walks the 64-row query
+//     tiles that can see the block, reading D and LSE * log2(e) of each
+//     tile's rows from the workspace; the next block's K/V rows are fetched
+//     during the current block's first tile.  S and
 //     dP come out of the MFMA with a lane per key and 16 query rows per lane,
 //     which is the B-operand layout of the dV^T and dK^T products; their A
 //     operands dO^T and Q^T are transposing LDS reads of the row-major tiles.
@@ -36,7 +38,8 @@
 //
 // Q/dO tiles (bwd_dkdv, three stages) and K/V tiles (bwd_dq, two stages) are
 // copied global -> LDS by buffer loads into XOR-swizzled stages (conflict-free
-// row and transposing reads, rows past N read as zero).
+// row and transposing reads, rows past N read as zero).  Gradients leave the
+// registers through free LDS stages and are stored as whole rows.
 #include <type_traits>
 
 #include "fa_common.hpp"
