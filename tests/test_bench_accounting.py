@@ -1,0 +1,39 @@
+"""CPU: the benchmark's FLOP accounting and its lookup of stored HBM counters."""
+
+import pytest
+
+import bench
+from io_aware_exact_24_amd.workloads import WORKLOADS, draw_workload
+
+
+def test_unmasked_pairs_per_workload():
+    w = WORKLOADS
+    # causal: N^2/2 per head; plain: N^2 per head
+    assert bench.unmasked_pairs(w[3], None) == 4 * 32 * 4096 * 4096 / 2
+    assert bench.unmasked_pairs(w[2], None) == 8 * 16 * 1024 * 1024
+    assert bench.unmasked_pairs(w[5], None) == 8 * 65536 * 65536 / 2
+    # key padding: N * L_b per head, summed over the batch
+    kl = draw_workload(w[4]).key_lens
+    assert bench.unmasked_pairs(w[4], kl) == 12 * 2048 * int(kl.sum())
+    assert 12 * 2048 * 16 * 512 <= bench.unmasked_pairs(w[4], kl) <= 12 * 2048 * 16 * 2048
+
+
+def test_metric_flops_match_the_convention():
+    f, b = bench.flops(4, 32, 4096, 128, True)
+    assert f == 4.0 * 4 * 32 * 4096 * 4096 * 128 / 2 and b == 2.5 * f
+    assert f == 4.0 * 128 * bench.unmasked_pairs(WORKLOADS[3], None)
+
+
+def test_stored_traffic_follows_the_kernel_digest(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    good, stale = bench.source_digest("bwd_dkdv_kernel"), "0" * 16
+    (prof / "traffic_decoder_causal.md").write_text(
+        "| kernel | source digest | read (MiB) | written (MiB) | total bytes per launch |\n"
+        "|---|---|---|---|---|\n"
+        f"| `bwd_dkdv_kernel` | `{good}` | 500.0 | 250.0 | 7.8643e+08 |\n"
+        f"| `fwd_bf16_kernel` | `{stale}` | 400.0 | 130.0 | 5.5574e+08 |\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.stored_traffic("bwd_dkdv_kernel") == pytest.approx(7.8643e8)
+    assert bench.stored_traffic("fwd_bf16_kernel") is None  # sources changed since
+    assert bench.stored_traffic("bwd_dq_kernel") is None    # no row
