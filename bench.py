@@ -241,6 +241,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shape", default=None, metavar="B,H,N,d[,causal]",
+                    help="time the step on another bf16 shape instead (counter sweeps; no CPU "
+                         "baseline)")
     ap.add_argument("--all-configs", action="store_true",
                     help="time forward and backward on every workload (one JSON line each) instead")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -262,6 +265,15 @@ def main():
     from io_aware_exact_24_amd.workloads import WORKLOADS, draw_workload
 
     w = WORKLOADS[WORKLOAD_NUMBER]
+    if args.shape:
+        import dataclasses
+
+        f = [int(x) for x in args.shape.split(",")]
+        if len(f) not in (4, 5):
+            raise SystemExit("--shape takes B,H,N,d or B,H,N,d,causal")
+        w = dataclasses.replace(w, number=0, name="custom", B=f[0], H=f[1], N=f[2], d=f[3],
+                                causal=bool(f[4]) if len(f) == 5 else True)
+        args.no_cpu_baseline = True
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = draw_workload(w)
@@ -351,8 +363,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decoder_causal: B=4 H=32 N=4096 d=128 causal bf16, N(0,1) inputs",
-                   "B": B, "H": H, "N": N, "d": d, "causal": True, "dropout_p": 0.0},
+        "config": {"workload": f"{w.name}: B={B} H={H} N={N} d={d}{' causal' if w.causal else ''} "
+                               "bf16, N(0,1) inputs",
+                   "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "dropout_p": 0.0},
         "fwd": {"ms": round(avg_fwd, 4), "tflops": round(ff / (avg_fwd * 1e-3) / 1e12, 2),
                 "frac_of_peak": round(ff / (avg_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "bwd": {"ms": round(avg_bwd, 4), "tflops": round(fb / (avg_bwd * 1e-3) / 1e12, 2),
