@@ -151,8 +151,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *   Q K^T and dP = dO V^T from Q, K, V and the saved normaliser (ML Canon 48
  *   FlashAttention, "backward without N x N"; Flash Attention hardware-aware
  *   optimisation, section 2.2).
- * fa_bwd_dkdv: dK and dV.  Each 128-key block is one workgroup that walks the
- *   query tiles, recomputing S and dP the same way.
+ * fa_bwd_dkdv: dK and dV.  Each 128-key block is walked over the query tiles
+ *   by one workgroup, recomputing S and dP the same way; the launch is
+ *   persistent (one workgroup per CU, each taking a chain of blocks).
  */
 fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
                             int B, int H, int N, int d, fa_dtype dtype,
