@@ -244,6 +244,8 @@ def main():
     ap.add_argument("--shape", default=None, metavar="B,H,N,d[,causal]",
                     help="time the step on another bf16 shape instead (counter sweeps; no CPU "
                          "baseline)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="run the forward as fa_fwd_split with this many key splits")
     ap.add_argument("--all-configs", action="store_true",
                     help="time forward and backward on every workload (one JSON line each) instead")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -295,10 +297,17 @@ def main():
         del src, dst
 
     names = ("fwd", "bwd_dq", "bwd_dkdv")
+    sws = None
+    if args.splits > 0:
+        sws = torch.empty(binding.fa_fwd_split_workspace_size(B, H, N, d, args.splits),
+                          dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         launches = (
-            lambda: binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, 0.0, 0, stream),
+            (lambda: binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, 0.0, 0, stream))
+            if sws is None else
+            (lambda: binding.fa_fwd_split(q, k, v, o, lse, w.scale, w.causal, None, 0.0, 0,
+                                          args.splits, sws, stream)),
             lambda: binding.fa_bwd_dq(q, k, v, o, do, lse, dq, w.scale, w.causal, None, 0.0, 0, ws,
                                       stream),
             lambda: binding.fa_bwd_dkdv(q, k, v, do, dk, dv, w.scale, w.causal, None, 0.0, 0, ws,
@@ -365,7 +374,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={B} H={H} N={N} d={d}{' causal' if w.causal else ''} "
                                "bf16, N(0,1) inputs",
-                   "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "dropout_p": 0.0},
+                   "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "dropout_p": 0.0,
+                   "fwd_splits": args.splits},
         "fwd": {"ms": round(avg_fwd, 4), "tflops": round(ff / (avg_fwd * 1e-3) / 1e12, 2),
                 "frac_of_peak": round(ff / (avg_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "bwd": {"ms": round(avg_bwd, 4), "tflops": round(fb / (avg_bwd * 1e-3) / 1e12, 2),

@@ -102,6 +102,30 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  hipStream_t stream);
 
 /*
+ * Split-KV forward: fa_fwd's result for small B*H, where one workgroup per
+ * query block would leave most of the GPU idle.  Each query block's key tiles
+ * are split num_splits ways (FlashAttention-2's better work partitioning,
+ * Flash Attention hardware-aware optimisation, section 4); every split runs
+ * the online softmax over its share and writes its fp32 O and LSE to the
+ * workspace, then a combine pass weights the splits by exp(LSE_s - LSE).
+ * Same arguments, checks and mask/dropout semantics as fa_fwd (bf16 only:
+ * FA_F32 is FA_ERR_UNSUPPORTED), plus
+ *   num_splits       1 .. FA_MAX_SPLITS (else FA_ERR_INVALID_ARG); splits
+ *                    that get no key tile are allowed and contribute nothing;
+ *   workspace        device buffer of at least
+ *                    fa_fwd_split_workspace_size() bytes, 16-byte aligned,
+ *                    contents irrelevant on entry, garbage on exit.
+ * The result equals fa_fwd's up to rounding (the softmax sums are taken in
+ * another order), not bitwise.
+ */
+#define FA_MAX_SPLITS 64
+size_t fa_fwd_split_workspace_size(int B, int H, int N, int d, fa_dtype dtype, int num_splits);
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                       const int32_t* key_lens, float dropout_p, uint64_t seed, int num_splits,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for these sizes: two fp32 [B, H, N]
  * row arrays, D_i = sum_k dO_ik O_ik and LSE_i * log2(e), each padded to a
  * multiple of 256 bytes.

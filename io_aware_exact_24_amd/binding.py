@@ -17,7 +17,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F32, FA_BF16 = 0, 1
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_bwd_preprocess",
-           "fa_bwd_dkdv", "fa_bwd_dq")
+           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_split", "fa_fwd_split_workspace_size")
+FA_MAX_SPLITS = 64
 
 _lib = None
 
@@ -47,6 +48,10 @@ def load_library():
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64,
                            vp, sz, vp]
+    lib.fa_fwd_split.restype = i
+    lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64, i, vp, sz, vp]
+    lib.fa_fwd_split_workspace_size.restype = sz
+    lib.fa_fwd_split_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -120,6 +125,47 @@ def fa_fwd(q, k, v, o, lse, scale, causal=False, key_lens=None, dropout_p=0.0, s
                     _stream(stream, q.device))
     if st != FA_OK:
         raise FaError(st, "fa_fwd")
+
+
+def fa_fwd_split_workspace_size(B, H, N, d, num_splits, dtype_code=FA_BF16):
+    return int(load_library().fa_fwd_split_workspace_size(B, H, N, d, dtype_code, num_splits))
+
+
+def fa_fwd_split(q, k, v, o, lse, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
+                 num_splits=2, workspace=None, stream=None):
+    """Enqueue the split-KV forward (bf16); o and lse are written.  workspace: a
+    uint8 device tensor of at least fa_fwd_split_workspace_size() bytes."""
+    import torch
+
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        _check(t, q.shape, q.dtype, q.device, name)
+    _check(q, q.shape, q.dtype, q.device, "q")
+    _check(lse, (B, H, N), torch.float32, q.device, "lse")
+    kl = _key_lens(key_lens, B, q.device)
+    if workspace is None:
+        raise ValueError("fa_fwd_split needs a workspace tensor (see fa_fwd_split_workspace_size)")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _dtype_code(q),
+                          float(scale), int(bool(causal)), _ptr(kl), float(dropout_p), int(seed),
+                          int(num_splits), _ptr(workspace), ws_bytes, _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_split")
+
+
+def forward_split(q, k, v, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0, num_splits=2,
+                  stream=None):
+    """Allocate O, LSE and the workspace with torch and call fa_fwd_split."""
+    import torch
+
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    nbytes = fa_fwd_split_workspace_size(B, H, N, d, num_splits, _dtype_code(q))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    fa_fwd_split(q, k, v, o, lse, scale, causal, key_lens, dropout_p, seed, num_splits, ws, stream)
+    return o, lse
 
 
 def fa_bwd_workspace_size(B, H, N, d, dtype_code=FA_BF16):

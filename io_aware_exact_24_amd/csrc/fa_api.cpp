@@ -37,23 +37,14 @@ size_t row_array_bytes(int B, int H, int N) {
   return (((size_t)B * H * N) * 4 + 255) & ~(size_t)255;
 }
 
-}  // namespace
+size_t pad256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-extern "C" {
-
-const char* fa_status_string(fa_status s) {
-  switch (s) {
-    case FA_OK: return "ok";
-    case FA_ERR_INVALID_ARG: return "invalid argument";
-    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
-    case FA_ERR_HIP: return "HIP launch error";
-  }
-  return "unknown status";
-}
-
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                 int N, int d, fa_dtype dtype, float scale, int causal, const int32_t* key_lens,
-                 float dropout_p, uint64_t seed, hipStream_t stream) {
+// fa_fwd (num_splits 0) and fa_fwd_split (num_splits >= 1, bf16 only, with a
+// workspace of fa_fwd_split_workspace_size bytes): checks, then the launch.
+fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int N, int d, fa_dtype dtype, float scale, int causal, const int32_t* key_lens,
+                  float dropout_p, uint64_t seed, int num_splits, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
   if (key_lens != nullptr && ((uintptr_t)key_lens & 3u) != 0) return FA_ERR_INVALID_ARG;
@@ -63,6 +54,12 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (dtype == FA_F32 && dropout_p > 0.0f) return FA_ERR_UNSUPPORTED;
+  if (num_splits > 0) {
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+    if (workspace_bytes < fa_fwd_split_workspace_size(B, H, N, d, dtype, num_splits))
+      return FA_ERR_INVALID_ARG;
+  }
 
   fa::FwdArgs a;
   a.q = q;
@@ -81,8 +78,52 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   a.drop_threshold = drop_threshold(dropout_p);
   a.drop_scale = drop_scale(dropout_p);
   a.seed = seed;
+  if (num_splits > 0) {
+    const size_t rows = (size_t)B * H * N;
+    a.num_splits = num_splits;
+    a.opart = (float*)workspace;
+    a.lsepart = (float*)((char*)workspace + pad256((size_t)num_splits * rows * d * 4));
+  }
   const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, stream) : fa::launch_fwd_f32(a, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, fa_dtype dtype, float scale, int causal, const int32_t* key_lens,
+                 float dropout_p, uint64_t seed, hipStream_t stream) {
+  return run_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, key_lens, dropout_p, seed, 0,
+                 nullptr, 0, stream);
+}
+
+size_t fa_fwd_split_workspace_size(int B, int H, int N, int d, fa_dtype dtype, int num_splits) {
+  if (elems(B, H, N, d) < 0 || (d != 64 && d != 128) || dtype != FA_BF16 || num_splits < 1 ||
+      num_splits > FA_MAX_SPLITS)
+    return 0;
+  const size_t rows = (size_t)B * H * N;
+  return pad256((size_t)num_splits * rows * d * 4) + pad256((size_t)num_splits * rows * 4);
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                       const int32_t* key_lens, float dropout_p, uint64_t seed, int num_splits,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_INVALID_ARG;
+  return run_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, key_lens, dropout_p, seed,
+                 num_splits, workspace, workspace_bytes, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype) {

@@ -49,6 +49,12 @@ struct FwdParams {
   uint32_t drop_threshold;
   float drop_scale;
   uint32_t seed_lo, seed_hi;
+  // Split-KV only: the key tiles of each query block are split num_splits
+  // ways; split s writes its normalised fp32 output and its LSE to
+  // opart[s][head][row][:] and lsepart[s][head][row] (head = b * H + h).
+  float* opart;
+  float* lsepart;
+  int num_splits, heads;
 };
 
 template <int D>
@@ -63,7 +69,7 @@ struct FwdCfg {
   static_assert(LOADS * THREADS == BN * CHUNKS, "tile/thread mismatch");
 };
 
-template <int D, bool CAUSAL, bool DROPOUT>
+template <int D, bool CAUSAL, bool DROPOUT, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdParams p) {
   using C = FwdCfg<D>;
@@ -85,18 +91,21 @@ void fwd_bf16_kernel(FwdParams p) {
   // With a causal mask query block b costs b + 1 key tiles: a workgroup takes
   // blocks nqb-1-w and w in turn, so every workgroup does the same work (no
   // stragglers at the end of the grid, half as many workgroup start-ups).
-  const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
+  // Split-KV: one query block per workgroup, the block's key tiles split
+  // num_splits ways (consecutive workgroups), costliest blocks first.
+  const int per_head = SPLIT ? nqb * p.num_splits : CAUSAL ? (nqb + 1) / 2 : nqb;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int head = lid / per_head;  // b * H + h
   const int w = lid - head * per_head;
-  const int nitems = CAUSAL && w != nqb - 1 - w ? 2 : 1;
+  const int nitems = !SPLIT && CAUSAL && w != nqb - 1 - w ? 2 : 1;
   const int bi = head / p.H, hi = head - bi * p.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
   for (int item = 0; item < nitems; ++item) {
   if (item) __syncthreads();  // every wave is done with the first block's tiles
-  const int qb = CAUSAL ? (item == 0 ? nqb - 1 - w : w) : w;
+  int qb = CAUSAL ? (item == 0 ? nqb - 1 - w : w) : w;
+  if constexpr (SPLIT) qb = CAUSAL ? nqb - 1 - w / p.num_splits : w / p.num_splits;
   const int q0 = qb * C::BM;
   const int qw = q0 + wave * 32;  // first query of this wave
   const int qi = qw + li;         // this lane's query
@@ -104,17 +113,27 @@ void fwd_bf16_kernel(FwdParams p) {
   int L = N;
   if (p.key_lens) L = min(max(p.key_lens[bi], 0), N);
   const int kend = CAUSAL ? min(L, q0 + C::BM) : L;  // keys [0, kend) matter to the workgroup
-  const int nkb = (kend + BN - 1) / BN;
+  int nkb = (kend + BN - 1) / BN;
   // Tiles [0, nfree) are unmasked for every query of the workgroup.
   int nfree = L / BN;
   if (CAUSAL) nfree = min(nfree, q0 / BN);
   nfree = min(nfree, nkb);
+  // Key tiles [jt0, jt0 + nkb) are this workgroup's; below, tile indices are
+  // relative to jt0 (0 unless the keys are split).
+  int jt0 = 0, split = 0;
+  if constexpr (SPLIT) {
+    split = w % p.num_splits;
+    const int nt = nkb;
+    jt0 = split * nt / p.num_splits;
+    nkb = (split + 1) * nt / p.num_splits - jt0;
+    nfree = min(max(nfree - jt0, 0), nkb);
+  }
 
   const size_t head_off = (size_t)head * N * D;
   const bf16* __restrict__ qg = p.q + head_off;
   // The copies cover the tiles [0, nkb) only: copies past them (issued without
   // a branch) read zeros without touching memory.
-  const uint32_t kv_bytes = (uint32_t)min(nkb * BN, N) * D * 2;
+  const uint32_t kv_bytes = (uint32_t)min((jt0 + nkb) * BN, N) * D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, kv_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, kv_bytes);
 
@@ -143,10 +162,10 @@ void fwd_bf16_kernel(FwdParams p) {
   }
   auto ld_off = [&](int i) { return ld_off0 + (uint32_t)(i * NW * 64 * 16); };
   auto issue_k_piece = [&](int jt, int stage, int i) {
-    lds_dma16(krs, kbuf(stage) + (i * NW + wave) * 512, ld_off(i) + (uint32_t)jt * (BN * D * 2));
+    lds_dma16(krs, kbuf(stage) + (i * NW + wave) * 512, ld_off(i) + (uint32_t)(jt0 + jt) * (BN * D * 2));
   };
   auto issue_v_piece = [&](int jt, int stage, int i) {
-    lds_dma16(vrs, vbuf(stage) + (i * NW + wave) * 512, ld_off(i) + (uint32_t)jt * (BN * D * 2));
+    lds_dma16(vrs, vbuf(stage) + (i * NW + wave) * 512, ld_off(i) + (uint32_t)(jt0 + jt) * (BN * D * 2));
   };
   auto issue_k = [&](int jt, int stage) {
 #pragma unroll
@@ -200,7 +219,7 @@ void fwd_bf16_kernel(FwdParams p) {
   };
   auto apply_mask = [&](int jt, f32x16 (&s)[2]) {
     // key = kb + key_of(t, r) with kb per lane; allowed iff key_of(t, r) < lim.
-    const int kb = jt * BN + 4 * hh;
+    const int kb = (jt0 + jt) * BN + 4 * hh;
     int lim = L - kb;
     if (CAUSAL) lim = min(lim, qi - kb + 1);
 #pragma unroll
@@ -336,7 +355,7 @@ void fwd_bf16_kernel(FwdParams p) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const uint32_t key4 = (uint32_t)(j * BN + 32 * t + 8 * g + 4 * hh);
+          const uint32_t key4 = (uint32_t)((jt0 + j) * BN + 32 * t + 8 * g + 4 * hh);
           const u32x4 w = philox(key4 >> 2, (uint32_t)qi, (uint32_t)hi, (uint32_t)bi, p.seed_lo,
                                  p.seed_hi);
 #pragma unroll
@@ -414,17 +433,33 @@ void fwd_bf16_kernel(FwdParams p) {
 
   // Epilogue: O = O^T / l, transposed through the K stages (free once every
   // wave is past the last tile) and written as whole rows; LSE = (mref +
-  // log2 l) * ln 2.
+  // log2 l) * ln 2.  A split writes its fp32 O and LSE for the combine pass.
   const float lt = pair_sum(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  __syncthreads();
-  {
-    bf16* ot = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
-    acc_rows_to_lds<D>(ot, oacc, inv, false, li, hh);
-    lds_rows_to_global<D>(ot, p.o + head_off + (size_t)qw * D, N - qw, lane);
-  }
-  if (qi < N && hh == 0) {
-    p.lse[(size_t)head * N + qi] = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
+  const float lse_out = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
+  if constexpr (SPLIT) {
+    const size_t prow = ((size_t)split * p.heads + head) * N + qi;
+    if (qi < N) {
+      float* orow = p.opart + prow * D;
+#pragma unroll
+      for (int u = 0; u < DU; ++u)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = oacc[u][4 * g + e] * inv;
+          *(f32x4*)(orow + 32 * u + 8 * g + 4 * hh) = ov;
+        }
+      if (hh == 0) p.lsepart[prow] = lse_out;
+    }
+  } else {
+    __syncthreads();
+    {
+      bf16* ot = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
+      acc_rows_to_lds<D>(ot, oacc, inv, false, li, hh);
+      lds_rows_to_global<D>(ot, p.o + head_off + (size_t)qw * D, N - qw, lane);
+    }
+    if (qi < N && hh == 0) p.lse[(size_t)head * N + qi] = lse_out;
   }
   }  // item
 }
@@ -499,20 +534,72 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
   }
 }
 
-template <int D, bool CAUSAL, bool DROPOUT>
+// Split-KV combine: O_i = sum_s w_s O_i^(s) / sum_s w_s with w_s = exp(LSE_i^(s) - m_i),
+// m_i = max_s LSE_i^(s), and LSE_i = m_i + ln sum_s w_s (each split's O is
+// normalised by its own row sum l_s, and exp(LSE^(s)) = l_s e^(m_s)).  Eight
+// columns per thread; a row whose splits all saw no key gets O = 0, LSE = -inf.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restrict__ opart,
+                                                          const float* __restrict__ lsepart,
+                                                          bf16* __restrict__ o,
+                                                          float* __restrict__ lse, int64_t rows,
+                                                          int splits) {
+  constexpr int LPR = D / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / LPR;
+  const int c = (int)(t % LPR);
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, lsepart[(int64_t)s * rows + row]);
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  float den = 0.0f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float ls = lsepart[(int64_t)s * rows + row];
+      if (ls == -INFINITY) continue;
+      const float wgt = __expf(ls - m);
+      den += wgt;
+      const float* src = opart + ((int64_t)s * rows + row) * D + 8 * c;
+      const f32x4 a = *(const f32x4*)src, b = *(const f32x4*)(src + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = fmaf(wgt, a[e], acc[e]);
+        acc[4 + e] = fmaf(wgt, b[e], acc[4 + e]);
+      }
+    }
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  bf16x8 ov;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ov[e] = (bf16)(acc[e] * inv);
+  *(bf16x8*)(o + row * D + 8 * c) = ov;
+  if (c == 0) lse[row] = den > 0.0f ? m + __logf(den) : -INFINITY;
+}
+
+template <int D, bool CAUSAL, bool DROPOUT, bool SPLIT>
 hipError_t launch_bf16(const FwdParams& p, int heads, hipStream_t s) {
   using C = FwdCfg<D>;
-  const int grid = heads * (CAUSAL ? (p.num_qblocks + 1) / 2 : p.num_qblocks);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROPOUT>), dim3(grid), dim3(C::THREADS), 0, s, p);
+  const int grid = heads * (SPLIT ? p.num_qblocks * p.num_splits
+                                  : CAUSAL ? (p.num_qblocks + 1) / 2 : p.num_qblocks);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROPOUT, SPLIT>), dim3(grid), dim3(C::THREADS), 0,
+                     s, p);
+  hipError_t e = hipGetLastError();
+  if (!SPLIT || e != hipSuccess) return e;
+  const int64_t rows = (int64_t)heads * p.N;
+  const int64_t threads = rows * (D / 8);
+  hipLaunchKernelGGL(fwd_combine_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     (const float*)p.opart, (const float*)p.lsepart, p.o, p.lse, rows, p.num_splits);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool SPLIT>
 hipError_t dispatch_bf16(const FwdParams& p, int heads, bool causal, bool dropout, hipStream_t s) {
   if (causal) {
-    return dropout ? launch_bf16<D, true, true>(p, heads, s) : launch_bf16<D, true, false>(p, heads, s);
+    return dropout ? launch_bf16<D, true, true, SPLIT>(p, heads, s)
+                   : launch_bf16<D, true, false, SPLIT>(p, heads, s);
   }
-  return dropout ? launch_bf16<D, false, true>(p, heads, s) : launch_bf16<D, false, false>(p, heads, s);
+  return dropout ? launch_bf16<D, false, true, SPLIT>(p, heads, s)
+                 : launch_bf16<D, false, false, SPLIT>(p, heads, s);
 }
 
 }  // namespace
@@ -534,12 +621,19 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   p.seed_hi = (uint32_t)(a.seed >> 32);
   const bool dropout = a.dropout_p > 0.0f;
   const int heads = a.B * a.H;
+  p.opart = a.opart;
+  p.lsepart = a.lsepart;
+  p.num_splits = a.num_splits;
+  p.heads = heads;
+  const bool split = a.num_splits > 0;
   if (a.d == 64) {
     p.num_qblocks = (a.N + FwdCfg<64>::BM - 1) / FwdCfg<64>::BM;
-    return dispatch_bf16<64>(p, heads, a.causal != 0, dropout, s);
+    return split ? dispatch_bf16<64, true>(p, heads, a.causal != 0, dropout, s)
+                 : dispatch_bf16<64, false>(p, heads, a.causal != 0, dropout, s);
   }
   p.num_qblocks = (a.N + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
-  return dispatch_bf16<128>(p, heads, a.causal != 0, dropout, s);
+  return split ? dispatch_bf16<128, true>(p, heads, a.causal != 0, dropout, s)
+               : dispatch_bf16<128, false>(p, heads, a.causal != 0, dropout, s);
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {

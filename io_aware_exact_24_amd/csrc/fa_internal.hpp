@@ -21,6 +21,12 @@ struct FwdArgs {
   uint32_t drop_threshold;  // floor(p * 2^32)
   float drop_scale;         // fp32(1 / (1 - p))
   uint64_t seed;
+  // Split-KV (bf16 only): num_splits > 0 splits each query block's key tiles
+  // that many ways into the fp32 workspaces opart [S][B*H][N][d] and
+  // lsepart [S][B*H][N], then combines them into o and lse.  0: one pass.
+  int num_splits = 0;
+  float* opart = nullptr;
+  float* lsepart = nullptr;
 };
 
 struct BwdArgs {

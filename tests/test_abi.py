@@ -157,3 +157,32 @@ def test_backward_compute_stages_check_scale_and_dropout(lib, kw):
 ])
 def test_backward_stages_reject_null(lib, name, stage):
     assert stage_calls(lib, null=name)[stage] == INVALID
+
+
+def split(lib, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, splits=2, ws=P, ws_bytes=None,
+          p=0.0, q=P):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_fwd_split_workspace_size(B, H, N, d, dtype, splits)
+    return lib.fa_fwd_split(q, P, P, P, P, B, H, N, d, dtype, 0.125, 1, None, p, 0, splits, ws,
+                            ws_bytes, None)
+
+
+def test_split_workspace_size():
+    ws = binding.fa_fwd_split_workspace_size
+    # fp32 partial O per split (padded to 256 B) then fp32 partial LSE per split
+    assert ws(2, 3, 100, 64, 4) == 4 * 2 * 3 * 100 * 64 * 4 + ((4 * 2 * 3 * 100 * 4 + 255) // 256) * 256
+    assert ws(1, 8, 4096, 128, 1) == 8 * 4096 * 128 * 4 + 8 * 4096 * 4
+    assert ws(1, 1, 128, 96, 2) == 0
+    assert ws(1, 1, 128, 64, 0) == 0
+    assert ws(1, 1, 128, 64, binding.FA_MAX_SPLITS + 1) == 0
+    assert ws(1, 1, 128, 64, 2, binding.FA_F32) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(splits=0), INVALID), (dict(splits=binding.FA_MAX_SPLITS + 1), INVALID),
+    (dict(dtype=binding.FA_F32), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+    (dict(ws=None), INVALID), (dict(ws=P + 8), INVALID), (dict(ws_bytes=16), INVALID),
+    (dict(q=None), INVALID), (dict(p=1.0), INVALID), (dict(N=0), INVALID),
+])
+def test_split_rejects(lib, kw, expect):
+    assert split(lib, **kw) == expect
