@@ -1,7 +1,8 @@
 """PyTorch autograd entry point over the C ABI (argument marshalling only).
 
-`flash_attention` runs fa_fwd in the forward of a torch.autograd.Function and
-fa_bwd in its backward, keeping only what the recompute backward needs: Q, K,
+`flash_attention` runs fa_fwd (fa_fwd_split when the shape has too few query
+blocks to fill the GPU) in the forward of a torch.autograd.Function and fa_bwd
+in its backward, keeping only what the recompute backward needs: Q, K,
 V, O and the per-row log-sum-exp (no N x N matrix; ML Canon 48 FlashAttention,
 "backward without N x N").  `scaled_dot_product_attention` takes the argument
 names of torch.nn.functional.scaled_dot_product_attention, the drop-in call the
@@ -30,12 +31,32 @@ def _from_bhnd(t, layout):
     return t if layout == "bhnd" else t.transpose(1, 2)
 
 
+def _splits(q, causal):
+    """Key splits for the forward: 2 (fa_fwd_split) when the plain forward
+    would launch fewer workgroups than the GPU has CUs (one per 128-query block,
+    causal ones in pairs), else 0 (fa_fwd).  bf16 on a GPU only."""
+    if q.dtype != torch.bfloat16 or not q.is_cuda:
+        return 0
+    B, H, N, _ = q.shape
+    blocks = (N + 127) // 128
+    workgroups = B * H * ((blocks + 1) // 2 if causal else blocks)
+    cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+    return 2 if workgroups < cus else 0
+
+
+def _forward(q, k, v, scale, causal, key_lens, dropout_p, seed):
+    s = _splits(q, causal)
+    if s:
+        return binding.forward_split(q, k, v, scale, causal, key_lens, dropout_p, seed, s)
+    return binding.forward(q, k, v, scale, causal, key_lens, dropout_p, seed)
+
+
 class FlashAttentionFunction(torch.autograd.Function):
     """O = softmax(mask(scale * Q K^T)) (with dropout) V on [B, H, N, d]."""
 
     @staticmethod
     def forward(ctx, q, k, v, scale, causal, key_lens, dropout_p, seed):
-        o, lse = binding.forward(q, k, v, scale, causal, key_lens, dropout_p, seed)
+        o, lse = _forward(q, k, v, scale, causal, key_lens, dropout_p, seed)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.key_lens = key_lens
         ctx.args = (scale, causal, dropout_p, seed)
@@ -73,8 +94,8 @@ def flash_attention(q, k, v, scale=None, causal=False, key_lens=None, dropout_p=
         o = FlashAttentionFunction.apply(qb, kb, vb, float(scale), bool(causal), key_lens,
                                          float(dropout_p), int(seed))
     else:
-        o, _ = binding.forward(qb, kb, vb, float(scale), bool(causal), key_lens, float(dropout_p),
-                               int(seed))
+        o, _ = _forward(qb, kb, vb, float(scale), bool(causal), key_lens, float(dropout_p),
+                        int(seed))
     return _from_bhnd(o, layout)
 
 

@@ -52,6 +52,26 @@ def test_autograd_matches_oracle(layout, causal, padded):
     assert eo <= TOL_O and max(errs) <= TOL_GRAD
 
 
+def test_small_shapes_take_the_split_forward():
+    # B*H*blocks below the CU count: the forward runs split in two; results
+    # equal fa_fwd_split's with S = 2 bit for bit and the oracle's within the bar
+    from io_aware_exact_24_amd.autograd import _splits
+
+    B, H, N, d = 1, 2, 1000, 128
+    inp = draw(B, H, N, d, torch.bfloat16, seed=80)
+    q, k, v = (leaf(t, "bhnd") for t in (inp.q, inp.k, inp.v))
+    assert _splits(q, True) == 2
+    o = flash_attention(q, k, v, causal=True)
+    o.backward(inp.dout.to(DEV))
+    o2, _ = binding.forward_split(q.detach(), k.detach(), v.detach(), d ** -0.5, True, None, 0.0, 0, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o2)
+    ro, _ = attention_forward(inp.q, inp.k, inp.v, float(np.float32(d ** -0.5)), True)
+    ref = attention_backward(inp.q, inp.k, inp.v, inp.dout, float(np.float32(d ** -0.5)), True)
+    assert max_abs(f64(o), ro) <= TOL_O
+    assert max(rel_l2(f64(t.grad), r) for t, r in zip((q, k, v), ref)) <= TOL_GRAD
+
+
 def test_autograd_equals_c_abi_calls_with_dropout():
     # the Function replays the forward's seed: results are the bits of
     # fa_fwd / fa_bwd called directly with that seed
@@ -62,7 +82,9 @@ def test_autograd_equals_c_abi_calls_with_dropout():
     o = flash_attention(q, k, v, causal=True, dropout_p=p, seed=seed)
     o.backward(do)
     qd, kd, vd = (t.detach() for t in (q, k, v))
-    o2, lse2 = binding.forward(qd, kd, vd, d ** -0.5, True, None, p, seed)
+    from io_aware_exact_24_amd.autograd import _forward
+
+    o2, lse2 = _forward(qd, kd, vd, d ** -0.5, True, None, p, seed)
     g2 = binding.backward(qd, kd, vd, o2, do, lse2, d ** -0.5, True, None, p, seed)
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), o2)
