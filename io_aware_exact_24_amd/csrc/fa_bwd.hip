@@ -777,6 +777,10 @@ void bwd_dq_kernel(BwdParams p) {
       const int m = i / KC, c = i % KC;
       return *(const bf16x8*)((m < 2 ? ks : vs) + roff[c] + (m & 1) * 32 * D);
     };
+    // Priority while this wave's exponentials and dS are on the critical
+    // path: the other workgroup's wave on the SIMD, in its dQ products,
+    // fills the gaps.
+    __builtin_amdgcn_s_setprio(3);
     ring[0] = sread(0);
     ring[1] = sread(1);
     __builtin_amdgcn_sched_barrier(0);
@@ -824,6 +828,7 @@ void bwd_dq_kernel(BwdParams p) {
     }
 
     // ---- dQ^T += K^T dS^T (contraction over the 64 keys)
+    __builtin_amdgcn_s_setprio(0);
     const lds_bf16* kt = to_lds(ks);
     constexpr int NQ = 4 * DU;  // index = (cc, u)
     auto tnext = [&](int i) {
