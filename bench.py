@@ -70,6 +70,29 @@ def stored_traffic(kernel):
     return float(m.group(2))
 
 
+def host_description():
+    """CPU model and the BLAS numpy was built against (the oracle's matmuls)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        import numpy as np
+
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # numpy without the dict form of show_config
+        pass
+    return model, blas
+
+
 def cpu_baseline(w, heads=CPU_SAMPLE_HEADS):
     """The oracle, untouched, on `heads` heads of the workload (forward +
     backward, one head at a time as it is written), timed on the host cores;
@@ -88,6 +111,7 @@ def cpu_baseline(w, heads=CPU_SAMPLE_HEADS):
     except AttributeError:
         cores = os.cpu_count()
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    model, blas = host_description()
     return {
         "value": (ff + fb) / dt / 1e12,
         "unit": "TFLOP/s",
@@ -96,6 +120,8 @@ def cpu_baseline(w, heads=CPU_SAMPLE_HEADS):
         "sample": f"{heads} heads (B=1, H={heads}, N={w.N}, d={w.d}, causal) of the workload, "
                   f"forward + backward, fp64 numpy, {dt:.1f} s wall",
         "seconds": round(dt, 2),
+        "cpu_model": model,
+        "blas": blas,
     }
 
 
@@ -162,6 +188,29 @@ def summarize_traffic(fetch_dir, write_dir, out_path):
     print("\n".join(lines))
 
 
+B2B_WARMUP, B2B_CALLS, B2B_REPEATS = 10, 50, 5
+
+
+def back_to_back_ms(fn, stream):
+    """Per-call time of `fn` (one enqueue on `stream`): B2B_WARMUP untimed
+    calls, then B2B_REPEATS runs of B2B_CALLS back-to-back calls between two
+    HIP events on the stream; the median run's time per call, in ms."""
+    import torch
+
+    for _ in range(B2B_WARMUP):
+        fn()
+    runs = []
+    for _ in range(B2B_REPEATS):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(B2B_CALLS):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        runs.append(ev[0].elapsed_time(ev[1]) / B2B_CALLS)
+    return sorted(runs)[len(runs) // 2]
+
+
 def unmasked_pairs(w, key_lens):
     """Unmasked (query, key) pairs of a workload, the unit of its FLOP count:
     N^2/2 per head with a causal mask (the N/2 diagonal pairs not counted), N * L_b per
@@ -175,9 +224,10 @@ def unmasked_pairs(w, key_lens):
 
 def all_configs(steps, warmup):
     """Time fa_fwd and fa_bwd on every workload (one JSON line each): inputs
-    resident on the GPU, HIP events around `steps` back-to-back calls on the
-    library's stream after `warmup` untimed ones.  A report, not the metric
-    line: forward FLOP = 4 d per unmasked pair, backward 2.5x the forward."""
+    resident on the GPU, back-to-back calls on the library's stream timed by
+    back_to_back_ms (10 warm-up calls, then the median of 5 runs of 50).  A
+    report, not the metric line: forward FLOP = 4 d per unmasked pair,
+    backward 2.5x the forward.  `steps` and `warmup` are not used."""
     import torch
 
     from io_aware_exact_24_amd import binding
@@ -188,15 +238,7 @@ def all_configs(steps, warmup):
     stream = torch.cuda.current_stream(dev)
 
     def timed(fn):
-        for _ in range(warmup):
-            fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for _ in range(steps):
-            fn()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / steps
+        return back_to_back_ms(fn, stream)
 
     for n, w in sorted(WORKLOADS.items()):
         inp = draw_workload(w)
@@ -248,6 +290,9 @@ def main():
                     help="run the forward as fa_fwd_split with this many key splits")
     ap.add_argument("--all-configs", action="store_true",
                     help="time forward and backward on every workload (one JSON line each) instead")
+    ap.add_argument("--step-only", action="store_true",
+                    help="skip the back-to-back pass timings (profiler runs); fwd/bwd then "
+                         "report the in-step times")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -335,6 +380,22 @@ def main():
 
     per = {n: sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps
            for i, n in enumerate(names)}
+
+    # Back-to-back calls of the forward alone and of the whole backward
+    # (fa_bwd), the timing protocol of the pass-level figures: the previous
+    # call's output, not the other pass's, is what the caches hold.
+    fwd_launch = (
+        (lambda: binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, 0.0, 0, stream))
+        if sws is None else
+        (lambda: binding.fa_fwd_split(q, k, v, o, lse, w.scale, w.causal, None, 0.0, 0,
+                                      args.splits, sws, stream)))
+    if args.step_only:
+        b2b_fwd, b2b_bwd = per["fwd"], per["bwd_dq"] + per["bwd_dkdv"]
+    else:
+        b2b_fwd = back_to_back_ms(fwd_launch, stream)
+        b2b_bwd = back_to_back_ms(
+            lambda: binding.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.scale, w.causal, None, 0.0, 0,
+                                   ws, stream), stream)
     avg_fwd = per["fwd"]
     avg_bwd = per["bwd_dq"] + per["bwd_dkdv"]
     ms_per_step = wall * 1e3 / args.steps
@@ -376,10 +437,21 @@ def main():
                                "bf16, N(0,1) inputs",
                    "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "dropout_p": 0.0,
                    "fwd_splits": args.splits},
-        "fwd": {"ms": round(avg_fwd, 4), "tflops": round(ff / (avg_fwd * 1e-3) / 1e12, 2),
-                "frac_of_peak": round(ff / (avg_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
-        "bwd": {"ms": round(avg_bwd, 4), "tflops": round(fb / (avg_bwd * 1e-3) / 1e12, 2),
-                "frac_of_peak": round(fb / (avg_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        # pass-level figures: back-to-back calls, median of 5 runs of 50
+        "fwd": {"ms": round(b2b_fwd, 4), "tflops": round(ff / (b2b_fwd * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(ff / (b2b_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "timing": "in-step" if args.step_only else
+                          "back-to-back fa_fwd: 10 warm-up, median of 5 x 50 calls"},
+        "bwd": {"ms": round(b2b_bwd, 4), "tflops": round(fb / (b2b_bwd * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(fb / (b2b_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "timing": "in-step" if args.step_only else
+                          "back-to-back fa_bwd: 10 warm-up, median of 5 x 50 calls"},
+        # the same passes inside the timed steps (forward after the previous
+        # step's backward)
+        "fwd_in_step": {"ms": round(avg_fwd, 4),
+                        "frac_of_peak": round(ff / (avg_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "bwd_in_step": {"ms": round(avg_bwd, 4),
+                        "frac_of_peak": round(fb / (avg_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "kernels_ms": {n: round(per[n], 4) for n in names},
         "roofline": roofline,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w),

@@ -50,7 +50,11 @@
  *                       element count overflows int64, non-finite or
  *                       non-positive scale, p outside [0, 1), workspace NULL
  *                       or smaller than fa_bwd_workspace_size().
- *   FA_ERR_UNSUPPORTED  d not in {64, 128}; fp32 with dropout; fp32 backward.
+ *   FA_ERR_UNSUPPORTED  d not in {64, 128}; fp32 with dropout; fp32 backward;
+ *                       one (b, h) slice of N * d elements of 2^32 bytes or
+ *                       more (N >= 2^24 at d = 128, N >= 2^25 at d = 64 in
+ *                       bf16): the kernels address a slice with 32-bit byte
+ *                       offsets.
  *   FA_ERR_HIP          a launch failed (hipGetLastError after launching).
  * key_lens lives in device memory and cannot be range-checked on the host; the
  * kernels clamp each L_b into [0, N].

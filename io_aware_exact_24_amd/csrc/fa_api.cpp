@@ -23,6 +23,14 @@ int64_t elems(int B, int H, int N, int d) {
   return n;
 }
 
+// The kernels address one (b, h) slice of a tensor through a buffer resource
+// whose byte range, and every tile offset inside it, is a 32-bit number: the
+// slice's N * d * element-size bytes must stay below 2^32.
+bool head_bytes_fit(int N, int d, fa_dtype dtype) {
+  const uint64_t elem = dtype == FA_F32 ? 4 : 2;
+  return (uint64_t)N * (uint64_t)d * elem < (1ull << 32);
+}
+
 bool valid_dropout(float p) { return isfinite(p) && p >= 0.0f && p < 1.0f; }
 
 uint32_t drop_threshold(float p) {
@@ -53,6 +61,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (!valid_dropout(dropout_p)) return FA_ERR_INVALID_ARG;
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!head_bytes_fit(N, d, dtype)) return FA_ERR_UNSUPPORTED;
   if (dtype == FA_F32 && dropout_p > 0.0f) return FA_ERR_UNSUPPORTED;
   if (num_splits > 0) {
     if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
@@ -111,7 +120,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 size_t fa_fwd_split_workspace_size(int B, int H, int N, int d, fa_dtype dtype, int num_splits) {
   if (elems(B, H, N, d) < 0 || (d != 64 && d != 128) || dtype != FA_BF16 || num_splits < 1 ||
-      num_splits > FA_MAX_SPLITS)
+      num_splits > FA_MAX_SPLITS || !head_bytes_fit(N, d, dtype))
     return 0;
   const size_t rows = (size_t)B * H * N;
   return pad256((size_t)num_splits * rows * d * 4) + pad256((size_t)num_splits * rows * 4);
@@ -128,7 +137,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype) {
   if (dtype != FA_BF16 || (d != 64 && d != 128)) return 0;
-  if (elems(B, H, N, d) < 0) return 0;
+  if (elems(B, H, N, d) < 0 || !head_bytes_fit(N, d, dtype)) return 0;
   return 2 * row_array_bytes(B, H, N);
 }
 
@@ -151,6 +160,7 @@ fa_status check_bwd(std::initializer_list<const void*> ptrs, const int32_t* key_
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!head_bytes_fit(N, d, dtype)) return FA_ERR_UNSUPPORTED;
   if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d, dtype)) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }

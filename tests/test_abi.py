@@ -96,6 +96,20 @@ def test_backward_rejects_null_tensor(lib, idx):
     assert bwd(lib, ptrs=ptrs) == INVALID
 
 
+@pytest.mark.parametrize("N,d", [(1 << 24, 128), (1 << 25, 64)])
+def test_per_head_byte_range_beyond_32_bits_is_unsupported(lib, N, d):
+    # one (b, h) slice of N * d bf16 elements reaches 2^32 bytes: the kernels'
+    # 32-bit buffer offsets could not address it, so every entry point refuses
+    # before any HIP call (the dummy pointers are never touched)
+    assert fwd(lib, N=N, d=d) == UNSUPPORTED
+    assert fwd(lib, N=N - 1, d=d, dtype=binding.FA_F32) == UNSUPPORTED  # fp32: 4 bytes each
+    assert split(lib, N=N, d=d, ws_bytes=1 << 62) == UNSUPPORTED
+    assert bwd(lib, N=N, d=d, ws_bytes=1 << 62) == UNSUPPORTED
+    assert set(stage_calls(lib, N=N, d=d, ws_bytes=1 << 62).values()) == {UNSUPPORTED}
+    assert lib.fa_bwd_workspace_size(1, 1, N, d, binding.FA_BF16) == 0
+    assert lib.fa_fwd_split_workspace_size(1, 1, N, d, binding.FA_BF16, 2) == 0
+
+
 def test_backward_rejects_short_workspace(lib):
     need = lib.fa_bwd_workspace_size(2, 3, 100, 128, binding.FA_BF16)
     assert bwd(lib, B=2, H=3, N=100, d=128, ws_bytes=need - 1) == INVALID

@@ -96,7 +96,17 @@ def test_threshold_and_scale():
     assert philox.dropout_threshold(0.5) == 1 << 31
     p32 = float(np.float32(0.1))
     assert philox.dropout_threshold(0.1) == math.floor(p32 * 2 ** 32)
-    assert philox.dropout_scale(0.1) == float(np.float32(1 / (1 - p32)))
+    # Literals, worked by hand: fp32(0.1) = 13421773 * 2^-27, so
+    # T = 13421773 * 2^5 = 429496736 exactly, and the keep scale
+    # 1 / (1 - p) = 2^27 / 120795955 = 1.11111111...4 rounds to the fp32 value
+    # 1.1111111640930176 (= 9320676 * 2^-23).
+    assert p32 == 13421773 * 2.0 ** -27
+    assert philox.dropout_threshold(0.1) == 429496736
+    assert philox.dropout_scale(0.1) == 1.1111111640930176
+    assert philox.dropout_scale(0.1) == 9320676 * 2.0 ** -23
+    assert philox.dropout_scale(0.5) == 2.0
+    assert philox.dropout_scale(0.25) == 1.3333333730697632  # 11184811 * 2^-23
+    assert philox.dropout_scale(0.0) == 1.0
     with pytest.raises(ValueError):
         philox.dropout_threshold(1.0)
 
