@@ -74,7 +74,8 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1,
   FA_ERR_UNSUPPORTED = 2,
-  FA_ERR_HIP = 3
+  FA_ERR_HIP = 3,
+  FA_ERR_TOO_LARGE = 4  /* fa_bwd_noalloc: sizes beyond its fixed scratch */
 } fa_status;
 
 typedef enum {
@@ -196,6 +197,32 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* d
                       float scale, int causal, const int32_t* key_lens, float dropout_p,
                       uint64_t seed, const void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments (minus the workspace), checks,
+ * results and determinism as fa_bwd, bit for bit: the same kernels run with
+ * the per-row terms kept in a fixed device array of FA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends.
+ *
+ * Limit: fa_bwd_workspace_size(B, H, N, d, dtype) <= FA_NOALLOC_SCRATCH_BYTES,
+ * i.e. B * H * N up to 4,194,304 query rows; larger sizes return
+ * FA_ERR_TOO_LARGE before any HIP call.  The device of `stream` (the current
+ * device for NULL) selects that device's array; its address is looked up
+ * once per device on the first call there (no allocation).
+ *
+ * Concurrency: every call on one device uses that device's single array.  Calls
+ * that can overlap on one device (different streams without ordering, or
+ * several host threads) race on it and give wrong gradients; order them on
+ * one stream or with events.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                         const int32_t* key_lens, float dropout_p, uint64_t seed,
+                         hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* fa_status_string(fa_status s);

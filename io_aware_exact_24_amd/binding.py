@@ -13,12 +13,14 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libfa.so"
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 FA_F32, FA_BF16 = 0, 1
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_bwd_preprocess",
-           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_split", "fa_fwd_split_workspace_size")
+           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_split", "fa_fwd_split_workspace_size",
+           "fa_bwd_noalloc")
 FA_MAX_SPLITS = 64
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -63,6 +65,9 @@ def load_library():
     lib.fa_bwd_dq.restype = i
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64, vp, sz,
                               vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f,
+                                   u64, vp]
     _lib = lib
     return lib
 
@@ -194,6 +199,28 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None
                     _stream(stream, q.device))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None,
+                   dropout_p=0.0, seed=0, stream=None):
+    """Enqueue the backward pass with the library's fixed device scratch instead
+    of a workspace (no allocation anywhere); dq, dk, dv are written.  Calls
+    that may overlap on one GPU race on that scratch."""
+    import torch
+
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, q.shape, q.dtype, q.device, name)
+    _check(q, q.shape, q.dtype, q.device, "q")
+    _check(lse, (B, H, N), torch.float32, q.device, "lse")
+    kl = _key_lens(key_lens, B, q.device)
+    st = lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                            _ptr(dk), _ptr(dv), B, H, N, d, _dtype_code(q), float(scale),
+                            int(bool(causal)), _ptr(kl), float(dropout_p), int(seed),
+                            _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_noalloc")
 
 
 def _bwd_common(q, tensors, lse, key_lens, workspace):

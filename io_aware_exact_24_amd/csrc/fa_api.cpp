@@ -1,9 +1,11 @@
 // C ABI of libfa.so: argument checks (all on the host, before any HIP call),
 // workspace sizing, and dispatch to the gfx950 kernel launchers.
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_internal.hpp"
@@ -107,6 +109,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration";
     case FA_ERR_HIP: return "HIP launch error";
+    case FA_ERR_TOO_LARGE: return "sizes exceed the fixed scratch of this entry point";
   }
   return "unknown status";
 }
@@ -244,6 +247,80 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, 
   if (st != FA_OK) return st;
   return run_bwd(q, k, v, o, dout, lse, dq, nullptr, nullptr, B, H, N, d, scale, causal, key_lens,
                  dropout_p, seed, workspace, fa::kBwdQ, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// fa_bwd_noalloc: fa_bwd with its per-row workspace in a fixed device array,
+// for callers that cannot allocate device memory.
+// ---------------------------------------------------------------------------
+
+// The backward's per-row terms (D, then LSE * log2(e)) for every call of
+// fa_bwd_noalloc on a device.  Each device holds its own copy at its own
+// address, kept until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: only the address returned by
+// hipGetSymbolAddress for a device may be handed to kernels.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` per device, once resolved
+
+// Device address of `scratch` on the device `stream` belongs to (the current
+// device for the NULL stream), resolved once per device with that device
+// current.
+fa_status scratch_for(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return FA_ERR_HIP;
+    dev = (int)d;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return FA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return FA_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return FA_ERR_HIP;
+    if (e != hipSuccess || ptr == nullptr) return FA_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                         const int32_t* key_lens, float dropout_p, uint64_t seed,
+                         hipStream_t stream) {
+  // Every argument check of fa_bwd, with the scratch standing in for the
+  // workspace (a placeholder address here: nothing is launched before the
+  // real one is known), then the size limit, all before any HIP call.
+  const size_t need = fa_bwd_workspace_size(B, H, N, d, dtype);
+  fa_status st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, key_lens, B, H, N, d, dtype, scale,
+                           dropout_p, kUnused, need);
+  if (st != FA_OK) return st;
+  if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  st = scratch_for(stream, &ws);
+  if (st != FA_OK) return st;
+  // The dQ stage writes D and LSE * log2(e) for every row before the dK/dV
+  // stage reads them (same stream), so nothing needs clearing.
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens, dropout_p,
+                 seed, ws, fa::kBwdAll, stream);
 }
 
 }  // extern "C"

@@ -48,6 +48,8 @@ def test_status_strings(lib):
     assert binding.fa_status_string(INVALID) == "invalid argument"
     assert binding.fa_status_string(UNSUPPORTED) == "unsupported configuration"
     assert binding.fa_status_string(binding.FA_ERR_HIP) == "HIP launch error"
+    assert binding.fa_status_string(binding.FA_ERR_TOO_LARGE) == \
+        "sizes exceed the fixed scratch of this entry point"
     assert binding.fa_status_string(42) == "unknown status"
 
 
@@ -200,3 +202,36 @@ def test_split_workspace_size():
 ])
 def test_split_rejects(lib, kw, expect):
     assert split(lib, **kw) == expect
+
+
+def noalloc(lib, ptrs=None, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, scale=0.125, p=0.0):
+    ptrs = ptrs or [P] * 9
+    return lib.fa_bwd_noalloc(*ptrs, B, H, N, d, dtype, scale, 0, None, p, 0, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=0), INVALID), (dict(scale=float("nan")), INVALID), (dict(p=1.0), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(dtype=binding.FA_F32), UNSUPPORTED),
+    (dict(N=1 << 24, d=128), UNSUPPORTED),
+    # one query row past the fixed scratch (2 x 4 bytes per row): refused on the
+    # host before any HIP call
+    (dict(B=1, H=1, N=(1 << 22) + 1), binding.FA_ERR_TOO_LARGE),
+    (dict(B=4, H=32, N=32768 + 64), binding.FA_ERR_TOO_LARGE),
+])
+def test_noalloc_rejects(lib, kw, expect):
+    assert noalloc(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("idx", range(9))
+def test_noalloc_rejects_null_tensor(lib, idx):
+    ptrs = [P] * 9
+    ptrs[idx] = None
+    assert noalloc(lib, ptrs=ptrs) == INVALID
+
+
+def test_noalloc_limit_is_the_workspace_of_4m_rows(lib):
+    # the largest accepted size fills the scratch exactly
+    assert lib.fa_bwd_workspace_size(1, 1, 1 << 22, 64, binding.FA_BF16) == \
+        binding.FA_NOALLOC_SCRATCH_BYTES
+    assert lib.fa_bwd_workspace_size(1, 1, (1 << 22) + 1, 64, binding.FA_BF16) > \
+        binding.FA_NOALLOC_SCRATCH_BYTES
