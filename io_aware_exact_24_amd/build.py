@@ -27,9 +27,15 @@ EXTRA = {"fa_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
+# The tile loops index register arrays (operand rings, accumulators) by the
+# loop counter and must unroll completely; a long body (the dropout variants
+# draw Philox numbers inside it) would otherwise pass LLVM's size limit for
+# "#pragma unroll", leave the loop rolled and turn every such index into a
+# chain of selects.
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-pragma-unroll-threshold=1000000",
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]

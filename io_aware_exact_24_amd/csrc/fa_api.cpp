@@ -26,11 +26,12 @@ int64_t elems(int B, int H, int N, int d) {
 }
 
 // The kernels address one (b, h) slice of a tensor through a buffer resource
-// whose byte range, and every tile offset inside it, is a 32-bit number: the
-// slice's N * d * element-size bytes must stay below 2^32.
-bool head_bytes_fit(int N, int d, fa_dtype dtype) {
+// whose byte range, and every tile offset inside it (rows up to 256 past the
+// last, for tiles fetched ahead), is a 32-bit number: (N + 256) rows of
+// `row_stride` elements must span fewer than 2^32 bytes.
+bool head_bytes_fit(int N, int64_t row_stride, fa_dtype dtype) {
   const uint64_t elem = dtype == FA_F32 ? 4 : 2;
-  return (uint64_t)N * (uint64_t)d * elem < (1ull << 32);
+  return ((uint64_t)N + 256) * (uint64_t)row_stride * elem <= (1ull << 32);
 }
 
 bool valid_dropout(float p) { return isfinite(p) && p >= 0.0f && p < 1.0f; }
@@ -78,6 +79,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   a.v = v;
   a.o = o;
   a.lse = lse;
+  a.sq = a.sk = a.sv = a.so = fa::contiguous_bhnd(H, N, d);
   a.B = B;
   a.H = H;
   a.N = N;
@@ -95,7 +97,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     a.opart = (float*)workspace;
     a.lsepart = (float*)((char*)workspace + pad256((size_t)num_splits * rows * d * 4));
   }
-  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, stream) : fa::launch_fwd_f32(a, stream);
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_16(a, stream) : fa::launch_fwd_f32(a, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -196,7 +198,8 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   // workspace: D, then LSE * log2(e)
   a.delta = (float*)workspace;
   a.lse2 = (float*)((char*)workspace + row_array_bytes(B, H, N));
-  const hipError_t e = fa::launch_bwd_bf16(a, stages, stream);
+  a.sq = a.sk = a.sv = a.so = a.sdo = a.sdq = a.sdk = a.sdv = fa::contiguous_bhnd(H, N, d);
+  const hipError_t e = fa::launch_bwd_16(a, stages, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

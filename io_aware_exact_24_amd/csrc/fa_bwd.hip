@@ -49,17 +49,19 @@ namespace fa {
 namespace {
 
 struct BwdParams {
-  const bf16* q;
-  const bf16* k;
-  const bf16* v;
-  const bf16* dout;
-  const bf16* o;       // forward output (read by the dQ kernel for D)
-  const float* lse;    // forward LSE (natural log; read by the dQ kernel)
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const void* o;       // forward output (read by the dQ kernel for D)
+  const float* lse;    // forward LSE, contiguous [B, H, N] (natural log; read by the dQ kernel)
   float* lse2;         // LSE * log2(e), +inf for rows without any allowed key
   float* delta;        // D
-  bf16* dq;
-  bf16* dk;
-  bf16* dv;
+  void* dq;
+  void* dk;
+  void* dv;
+  // element strides (batch, head, row) of each tensor; d is contiguous
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   const int32_t* key_lens;
   int H, N, num_blocks;
   int units;  // dK/dV work units (blocks, or causal pairs of blocks) over all heads
@@ -78,7 +80,7 @@ using P1 = std::integral_constant<int, 1>;
 __device__ __forceinline__ float dropout_z(const BwdParams& p, int row, int key, int hi, int bi) {
   const u32x4 w = philox((uint32_t)key >> 2, (uint32_t)row, (uint32_t)hi, (uint32_t)bi, p.seed_lo,
                          p.seed_hi);
-  const uint32_t word = (key & 3) == 0 ? w[0] : (key & 3) == 1 ? w[1] : (key & 3) == 2 ? w[2] : w[3];
+  const uint32_t word = philox_word(w, key);
   return word >= p.drop_threshold ? p.drop_scale : 0.0f;
 }
 
@@ -116,8 +118,7 @@ __device__ __forceinline__ uint32_t quad_keep4(const BwdParams& p, int row0, int
     constexpr int j = decltype(j_t)::value;
     // Lane q reads lane (q + j) & 3, which sends word (sender - j) & 3 = q of
     // its row's counter: this lane's key at row row0 + ((q + j) & 3).
-    const int idx = (q - j) & 3;
-    const uint32_t send = idx == 0 ? w[0] : idx == 1 ? w[1] : idx == 2 ? w[2] : w[3];
+    const uint32_t send = philox_word(w, q - j);
     constexpr int ctrl = (j & 3) | (((1 + j) & 3) << 2) | (((2 + j) & 3) << 4) | (((3 + j) & 3) << 6);
     const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, ctrl, 0xF, 0xF, false);
     bits |= (uint32_t)(got >= p.drop_threshold) << ((q + j) & 3);
@@ -136,10 +137,13 @@ __device__ __forceinline__ uint32_t quad_keep4(const BwdParams& p, int row0, int
 //   phase 3: dP_{t+1} = dO_{t+1} V^T  | P_{t+1} of rows 32..63
 // Tiles t (transposing reads) and t+1 (row reads) are read while tile t+2 is
 // copied, so Q, dO, LSE*log2e and D have three LDS stages.
-template <int D, bool CAUSAL, bool DROPOUT>
+template <typename E, int D, bool CAUSAL, bool DROPOUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p) {
   using C = KvCfg<D>;
+  using V8 = typename Elem<E>::v8;
+  using V4 = typename Elem<E>::v4;
+  constexpr int ES = 2;
   constexpr int BQ = C::BQ, NW = C::NW, TILE = C::TILE, BK = C::BK;
   constexpr int KC = D / 16;  // k-steps of the S and dP products
   constexpr int DU = D / 32;  // 32-wide blocks of the head dimension
@@ -147,12 +151,12 @@ void bwd_dkdv_kernel(BwdParams p) {
   static_assert(NP == 4 * DU, "phase sizes");
   constexpr int PD = 4;       // operand reads run PD MFMAs ahead
   constexpr int RG = 8;       // ring slots (divides every body's MFMA count)
-  __shared__ __attribute__((aligned(1024))) bf16 sq0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 so0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sq1[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 so1[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sq2[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 so2[TILE];
+  __shared__ __attribute__((aligned(1024))) E sq0[TILE];
+  __shared__ __attribute__((aligned(1024))) E so0[TILE];
+  __shared__ __attribute__((aligned(1024))) E sq1[TILE];
+  __shared__ __attribute__((aligned(1024))) E so1[TILE];
+  __shared__ __attribute__((aligned(1024))) E sq2[TILE];
+  __shared__ __attribute__((aligned(1024))) E so2[TILE];
   __shared__ __attribute__((aligned(256))) float sl0[BQ];
   __shared__ __attribute__((aligned(256))) float sl1[BQ];
   __shared__ __attribute__((aligned(256))) float sl2[BQ];
@@ -161,12 +165,12 @@ void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float sd2[BQ];
   // K rows of the workgroup's key block (two 64-row tiles), copied in at the
   // start of each block; its V rows go to stage 2 until the first body.
-  __shared__ __attribute__((aligned(1024))) bf16 skv[2 * TILE];
-  auto qst = [&](auto s) __attribute__((always_inline)) -> bf16* {
+  __shared__ __attribute__((aligned(1024))) E skv[2 * TILE];
+  auto qst = [&](auto s) __attribute__((always_inline)) -> E* {
     constexpr int S = decltype(s)::value;
     return S == 0 ? sq0 : S == 1 ? sq1 : sq2;
   };
-  auto ost = [&](auto s) __attribute__((always_inline)) -> bf16* {
+  auto ost = [&](auto s) __attribute__((always_inline)) -> E* {
     constexpr int S = decltype(s)::value;
     return S == 0 ? so0 : S == 1 ? so1 : so2;
   };
@@ -212,7 +216,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int li = lane & 31, hh = lane >> 5;
   // The next block's K rows (this lane's key) land here and its V rows in skv
   // during the current block's first tile.
-  bf16x8 knext[KC];
+  V8 knext[KC];
   bool prefetched = false, started = false;
   while (u < uend) {
   if (started) __syncthreads();  // every wave is done with the previous block's LDS
@@ -238,7 +242,11 @@ void bwd_dkdv_kernel(BwdParams p) {
   int L = N;
   if (p.key_lens) L = min(max(p.key_lens[bi], 0), N);
 
-  const size_t head_off = (size_t)head * N * D;
+  // (b, h) slices through per-tensor strides
+  const E* qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h);
+  const E* dog = (const E*)p.dout + (bi * p.sdo.b + hi * p.sdo.h);
+  E* dkg = (E*)p.dk + (bi * p.sdk.b + hi * p.sdk.h);
+  E* dvg = (E*)p.dv + (bi * p.sdv.b + hi * p.sdv.h);
 
   // dV^T / dK^T tile u, register r -> d = 32u + 8(r/4) + 4hh + r%4; the first
   // product into each defines it.
@@ -249,11 +257,11 @@ void bwd_dkdv_kernel(BwdParams p) {
   if (kb >= L) {  // every key of the block is padding
     prefetched = false;  // the next block's rows are fetched at its start
     if (key < N) {
-      const bf16x4 z = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+      const V4 z = {(E)0.0f, (E)0.0f, (E)0.0f, (E)0.0f};
 #pragma unroll
       for (int c = 0; c < D / 4; c += 2) {
-        *(bf16x4*)(p.dk + head_off + (size_t)key * D + 4 * c + 4 * hh) = z;
-        *(bf16x4*)(p.dv + head_off + (size_t)key * D + 4 * c + 4 * hh) = z;
+        *(V4*)(dkg + (int64_t)key * p.sdk.n + 4 * c + 4 * hh) = z;
+        *(V4*)(dvg + (int64_t)key * p.sdv.n + 4 * c + 4 * hh) = z;
       }
     }
     continue;
@@ -261,41 +269,52 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   // K and V rows of this lane's key as B operands (k = head dimension),
   // read from LDS after the block's rows have been copied in.
-  bf16x8 kreg[KC], vreg[KC];
+  V8 kreg[KC], vreg[KC];
 
   // Copies of Q and dO tiles with LSE*log2e and D (rows past N read as zero).
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q + head_off, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.dout + head_off, (uint32_t)N * D * 2);
+  const int sqn = (int)p.sq.n, son_ = (int)p.sdo.n, skn = (int)p.sk.n, svn = (int)p.sv.n;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qg, rows_bytes(N, sqn, D, ES));
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(dog, rows_bytes(N, son_, D, ES));
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lse2 + (size_t)head * N, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.delta + (size_t)head * N, (uint32_t)N * 4);
   // Copy i of this lane fills chunk slot (i * NW + wave) * 64 + lane: row
-  // r = (i * NW + wave) * 64 / CHUNKS + lane / CHUNKS, chunk lane % CHUNKS.
-  // The swizzle of r depends on r mod 16 only, which does not change with i,
-  // so copy i is copy 0 shifted by i * NW * 64 chunks.
-  static_assert((NW * 64 / C::CHUNKS) % 16 == 0, "copy rows must keep their swizzle");
-  uint32_t ld_off0;
+  // r = i * COPY_ROWS + wave * 64 / CHUNKS + lane / CHUNKS, chunk
+  // lane % CHUNKS.  The swizzle of r depends on r mod 16 only, which does not
+  // change with i, so copy i is copy 0 moved by i * COPY_ROWS rows.  Per
+  // tensor, the lane's part of the byte offset is ldl_*; the rest is
+  // wave-uniform and is added to it.
+  constexpr int COPY_ROWS = NW * 64 / C::CHUNKS;
+  static_assert(COPY_ROWS % 16 == 0, "copy rows must keep their swizzle");
+  const int wrow = wave * 64 / C::CHUNKS;  // wave's first row of a copy round
+  uint32_t ldl_q, ldl_o;
   {
-    const int r = wave * 64 / C::CHUNKS + lane / C::CHUNKS, pc = lane % C::CHUNKS;
-    ld_off0 = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
+    const int r = wrow + lane / C::CHUNKS, pc = lane % C::CHUNKS;
+    const int lch = (pc ^ swz<D>(r)) * 8;
+    ldl_q = (uint32_t)((lane / C::CHUNKS) * sqn + lch) * ES;
+    ldl_o = (uint32_t)((lane / C::CHUNKS) * son_ + lch) * ES;
   }
   // K rows of block (head at hoff, first key kb_) straight into registers
   // (this lane's key, rows past N read as zero), V rows into skv with the
   // tiles' coalesced copy pattern: KC + 2 * LOADS memory operations.
   constexpr int NFETCH = KC + 2 * C::LOADS;
-  auto fetch_kv = [&](size_t hoff, int kb_, bf16x8 (&kdst)[KC]) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + hoff, (uint32_t)N * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + hoff, (uint32_t)N * D * 2);
-    const uint32_t krow = (uint32_t)(kb_ + 32 * wave + li) * (D * 2) + (uint32_t)(16 * hh);
+  auto fetch_kv = [&](int head_, int kb_, V8 (&kdst)[KC]) __attribute__((always_inline)) {
+    const int b_ = head_ / p.H, h_ = head_ - b_ * p.H;
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc((const E*)p.k + (b_ * p.sk.b + h_ * p.sk.h), rows_bytes(N, skn, D, ES));
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc((const E*)p.v + (b_ * p.sv.b + h_ * p.sv.h), rows_bytes(N, svn, D, ES));
+    const uint32_t krow = (uint32_t)(min(kb_ + 32 * wave + li, N) * skn) * ES + (uint32_t)(16 * hh);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      kdst[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, krow + 32 * c, 0, 0));
-    const int kt0 = kb_ / BQ;
+      kdst[c] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(krs, krow + 32 * c, 0, 0));
+    const int r = wrow + lane / C::CHUNKS, pc = lane % C::CHUNKS;
+    const uint32_t ldl_v = (uint32_t)((lane / C::CHUNKS) * svn + (pc ^ swz<D>(r)) * 8) * ES;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i)
-        lds_dma16(vrs, skv + h * TILE + (i * NW + wave) * 512,
-                  ld_off0 + (uint32_t)(kt0 + h) * (BQ * D * 2) + (uint32_t)(i * NW * 64 * 16));
+        lds_dma16_row(vrs, skv + h * TILE + (i * NW + wave) * 512, ldl_v, kb_ + h * BQ + i * COPY_ROWS + wrow,
+                      (uint32_t)svn * ES);
   };
 
   // Copy piece x of tile `it` into stage s: pieces 0 .. 2*LOADS-1 are this
@@ -307,11 +326,11 @@ void bwd_dkdv_kernel(BwdParams p) {
     constexpr int x = decltype(x_t)::value;
     if constexpr (x < 2 * C::LOADS) {
       constexpr int i = x / 2;
-      const uint32_t off = ld_off0 + (uint32_t)it * (BQ * D * 2) + (uint32_t)(i * NW * 64 * 16);
+      const int row0 = it * BQ + i * COPY_ROWS + wrow;  // wave-uniform
       if constexpr (x % 2 == 0)
-        lds_dma16(qrs, qst(s) + (i * NW + wave) * 512, off);
+        lds_dma16_row(qrs, qst(s) + (i * NW + wave) * 512, ldl_q, row0, (uint32_t)sqn * ES);
       else
-        lds_dma16(ors, ost(s) + (i * NW + wave) * 512, off);
+        lds_dma16_row(ors, ost(s) + (i * NW + wave) * 512, ldl_o, row0, (uint32_t)son_ * ES);
     } else {
       const bool dv = wave >= 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(dv ? drs : lrs, (lds_void_t*)(dv ? dst(s) : lst(s)), 4,
@@ -343,14 +362,14 @@ void bwd_dkdv_kernel(BwdParams p) {
       const int r = trow + 8 * half;
       toff[half][u] = r * D + (((4 * u + (tcol >> 3)) ^ swz<D>(r)) * 8) + (tcol & 7);
     }
-  auto row_read = [&](const bf16* base, int a, int c) __attribute__((always_inline)) {
-    return *(const bf16x8*)(base + roff[c] + a * 32 * D);
+  auto row_read = [&](const E* base, int a, int c) __attribute__((always_inline)) {
+    return *(const V8*)(base + roff[c] + a * 32 * D);
   };
-  auto tr_read = [&](const bf16* base, int kc, int u) __attribute__((always_inline)) {
-    const lds_bf16* b = to_lds(base);
-    const bf16x4 lo = lds_read_tr4(b + toff[0][u] + 16 * kc * D);
-    const bf16x4 h4 = lds_read_tr4(b + toff[1][u] + 16 * kc * D);
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
+  auto tr_read = [&](const E* base, int kc, int u) __attribute__((always_inline)) {
+    const lds_bf16* b = (const lds_bf16*)base;
+    const V4 lo = __builtin_bit_cast(V4, lds_read_tr4(b + toff[0][u] + 16 * kc * D));
+    const V4 h4 = __builtin_bit_cast(V4, lds_read_tr4(b + toff[1][u] + 16 * kc * D));
+    return V8{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
   };
   // Per-row values of group g (rows 8g + 4hh .. +3) of row half a.
   auto rows4 = [&](const float* base, int grp) __attribute__((always_inline)) {
@@ -365,15 +384,15 @@ void bwd_dkdv_kernel(BwdParams p) {
   // as B chunks (chunk kc holds rows 16kc + 8(x/4) + 4hh + x%4 in slot x), the
   // dropout keep bits, and the operand ring.
   f32x16 sp[2], sdp[2];
-  bf16x8 spb[4];
+  V8 spb[4];
   uint32_t zb = 0;
-  bf16x8 ring[RG];
+  V8 ring[RG];
   const f32x16 zero = {};
 
   // P of element pair (k, k+1) of tile `it` from its scores (in place in s),
   // packed into pb; k = 16a + r, rows 32a + 8(r/4) + 4hh + r%4.
   // Allowed iff the row offset within the tile is at least lo (and only then).
-  auto exp_pair = [&](int it, f32x16 (&s)[2], bf16x8 (&pb)[4], uint32_t& zn, int k,
+  auto exp_pair = [&](int it, f32x16 (&s)[2], V8 (&pb)[4], uint32_t& zn, int k,
                       const f32x4& l4, int lo, auto masked_t) {
     constexpr bool MASKED = decltype(masked_t)::value;
     const int a = k >> 4, r = k & 15, g = r >> 2, e = r & 3;
@@ -390,22 +409,22 @@ void bwd_dkdv_kernel(BwdParams p) {
         const bool keep = (zn >> (k + x)) & 1;
         pt = keep ? pv * p.drop_scale : 0.0f;
       }
-      pb[2 * a + (g >> 1)][4 * (g & 1) + e + x] = (bf16)pt;
+      pb[2 * a + (g >> 1)][4 * (g & 1) + e + x] = (E)pt;
     }
-    pin(pb[2 * a + (g >> 1)]);  // keep the work beside this MFMA
+    pin_v(pb[2 * a + (g >> 1)]);  // keep the work beside this MFMA
   };
   // Row-offset bound of the causal mask for tile `it` (see exp_pair).
   auto mask_lo = [&](int it) __attribute__((always_inline)) { return key - it * BQ - 4 * hh; };
   // dS of element pair (k, k+1) of the current tile into dsb.
-  auto ds_pair = [&](bf16x8 (&dsb)[4], int k, const f32x4& d4) {
+  auto ds_pair = [&](V8 (&dsb)[4], int k, const f32x4& d4) {
     const int a = k >> 4, r = k & 15, g = r >> 2, e = r & 3;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       float dp = sdp[a][r + x];
       if constexpr (DROPOUT) dp = ((zb >> (k + x)) & 1) ? dp * p.drop_scale : 0.0f;
-      dsb[2 * a + (g >> 1)][4 * (g & 1) + e + x] = (bf16)(sp[a][r + x] * (dp - d4[e + x]));
+      dsb[2 * a + (g >> 1)][4 * (g & 1) + e + x] = (E)(sp[a][r + x] * (dp - d4[e + x]));
     }
-    pin(dsb[2 * a + (g >> 1)]);  // keep the work beside this MFMA
+    pin_v(dsb[2 * a + (g >> 1)]);  // keep the work beside this MFMA
   };
 
   // ---- prologue: tiles it0 (stage 0) and it0 + 1 (stage 1); S, dP and P of
@@ -414,7 +433,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) kreg[c] = knext[c];
   } else {
-    fetch_kv(head_off, kb, kreg);
+    fetch_kv(head, kb, kreg);
   }
   issue_tile(it0, Stage<0>{});
   issue_tile(it0 + 1, Stage<1>{});
@@ -425,19 +444,19 @@ void bwd_dkdv_kernel(BwdParams p) {
   __syncthreads();
   {
     // V rows 32 * wave .. +31 of the block: 64-row tile wave / 2, half wave % 2.
-    const bf16* vt = skv + (wave >> 1) * TILE;
+    const E* vt = skv + (wave >> 1) * TILE;
 #pragma unroll
     for (int c = 0; c < KC; ++c) vreg[c] = row_read(vt, wave & 1, c);
   }
   {
-    const bf16* q = qst(Stage<0>{});
-    const bf16* o = ost(Stage<0>{});
+    const E* q = qst(Stage<0>{});
+    const E* o = ost(Stage<0>{});
     constexpr int NS = 2 * NP;  // S halves, then dP halves
     auto pread = [&](int i) __attribute__((always_inline)) {
       const int m = i / KC, c = i % KC;
       return row_read(m < 2 ? q : o, m & 1, c);
     };
-    bf16x8 pr[3];
+    V8 pr[3];
     pr[0] = pread(0);
     pr[1] = pread(1);
 #pragma unroll
@@ -445,7 +464,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       if (i + 2 < NS) pr[(i + 2) % 3] = pread(i + 2);
       const int m = i / KC, c = i % KC;
       f32x16& acc = m < 2 ? sp[m & 1] : sdp[m & 1];
-      acc = mfma32(pr[i % 3], m < 2 ? kreg[c] : vreg[c], c == 0 ? zero : acc);
+      acc = Elem<E>::mma(pr[i % 3], m < 2 ? kreg[c] : vreg[c], c == 0 ? zero : acc);
     }
     const float* ls = lst(Stage<0>{});
     const int lo = mask_lo(it0);
@@ -468,16 +487,16 @@ void bwd_dkdv_kernel(BwdParams p) {
     using S1 = Stage<S + 1>;
     using S2 = Stage<S + 2>;
     constexpr int NOPS = 4 * NP;
-    const bf16* qt = qst(s_t);
-    const bf16* ot = ost(s_t);
-    const bf16* qn = qst(S1{});
-    const bf16* on = ost(S1{});
+    const E* qt = qst(s_t);
+    const E* ot = ost(s_t);
+    const E* qn = qst(S1{});
+    const E* on = ost(S1{});
     const float* dt = dst(s_t);
     const float* ln = lst(S1{});
     __syncthreads();  // tile t+1 resident; every wave is done with tile t-1
 
     // A operand of MFMA i of this body; i >= NOPS: of the next body's first ones.
-    auto aread = [&](auto i_t) __attribute__((always_inline)) -> bf16x8 {
+    auto aread = [&](auto i_t) __attribute__((always_inline)) -> V8 {
       constexpr int i = decltype(i_t)::value;
       constexpr int ph = i / NP, j = i % NP;
       if constexpr (i >= NOPS) return tr_read(on, (i - NOPS) / DU, (i - NOPS) % DU);
@@ -487,7 +506,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       else return row_read(on, j / KC, j % KC);
     };
     f32x16 sn[2], pn[2];
-    bf16x8 dsb[4], pbn[4];
+    V8 dsb[4], pbn[4];
     uint32_t zn = 0;
     const int lo = mask_lo(t + 1);
     // elementwise work: dS pairs during phases 0-1, P pairs during phases 2-3,
@@ -520,21 +539,21 @@ void bwd_dkdv_kernel(BwdParams p) {
       if constexpr (i % 2 == 0 && i / 2 < NPIECE)
         issue_piece(t + 2, S2{}, std::integral_constant<int, i / 2>{});
       constexpr int ph = i / NP, j = i % NP;
-      const bf16x8& a = ring[i % RG];
+      const V8& a = ring[i % RG];
       if constexpr (ph == 0) {
         if constexpr (FIRST && j / DU == 0)
-          mfma32_acc_first(dvacc[j % DU], a, spb[j / DU]);
+          Elem<E>::mma_acc_first(dvacc[j % DU], a, spb[j / DU]);
         else
-          mfma32_acc(dvacc[j % DU], a, spb[j / DU]);
+          Elem<E>::mma_acc(dvacc[j % DU], a, spb[j / DU]);
       } else if constexpr (ph == 1) {
-        sn[j / KC] = mfma32(a, kreg[j % KC], j % KC == 0 ? zero : sn[j / KC]);
+        sn[j / KC] = Elem<E>::mma(a, kreg[j % KC], j % KC == 0 ? zero : sn[j / KC]);
       } else if constexpr (ph == 2) {
         if constexpr (FIRST && j / DU == 0)
-          mfma32_acc_first(dkacc[j % DU], a, dsb[j / DU]);
+          Elem<E>::mma_acc_first(dkacc[j % DU], a, dsb[j / DU]);
         else
-          mfma32_acc(dkacc[j % DU], a, dsb[j / DU]);
+          Elem<E>::mma_acc(dkacc[j % DU], a, dsb[j / DU]);
       } else {
-        pn[j / KC] = mfma32(a, vreg[j % KC], j % KC == 0 ? zero : pn[j / KC]);
+        pn[j / KC] = Elem<E>::mma(a, vreg[j % KC], j % KC == 0 ? zero : pn[j / KC]);
       }
       // the operands of the AccVGPR-form MFMAs of ops i-1 .. i-3 stay live
       // until here: the MFMAs of two later ops (whole groups before this one)
@@ -542,8 +561,8 @@ void bwd_dkdv_kernel(BwdParams p) {
       static_for<3>([&](auto d_t) __attribute__((always_inline)) {
         constexpr int k = i - 1 - decltype(d_t)::value, kph = k / NP, kj = k % NP;
         if constexpr (k >= 0 && (kph == 0 || kph == 2)) {
-          keep(ring[k % RG]);
-          keep(kph == 0 ? spb[kj / DU] : dsb[kj / DU]);
+          keep_v(ring[k % RG]);
+          keep_v(kph == 0 ? spb[kj / DU] : dsb[kj / DU]);
         }
       });
       valu(i_t);
@@ -562,7 +581,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       // stay in flight until the end of the next body (skv is free: every
       // wave read its V rows before this body's barrier).  Not with dropout,
       // whose keep-mask state leaves no registers for them.
-      fetch_kv((size_t)nhead * N * D, njb * BK, knext);
+      fetch_kv(nhead, njb * BK, knext);
       wait_vmem_le<NFETCH>();  // tile t+2 landed (this wave's share)
     } else {
       wait_vmem();  // tile t+2 landed (this wave's share) before the next barrier
@@ -581,20 +600,26 @@ void bwd_dkdv_kernel(BwdParams p) {
     if (t + 2 >= nit) break;
     body(t + 2, Stage<0>{}, F_{}, F_{});
   }
-  acc_settle();
+  // the last accumulate MFMAs complete before the VALU reads dK^T and dV^T
+  settle_acc(dkacc[0]);
+#pragma unroll
+  for (int u = 0; u < DU; ++u) {
+    if (u) tie_acc(dkacc[u]);
+    tie_acc(dvacc[u]);
+  }
   // dK = scale * dK^T^T and dV through LDS (stages 0 and 1 are free once every
   // wave is past the last tile), then whole rows to memory.  Keys past the key
   // length get zeros; rows past N are not written.
   __syncthreads();
   {
     const bool zero = key >= L;
-    bf16* kt = ((wave >> 1) ? so0 : sq0) + (wave & 1) * 32 * D;
-    bf16* vt = ((wave >> 1) ? so1 : sq1) + (wave & 1) * 32 * D;
-    acc_rows_to_lds<D>(kt, dkacc, p.scale, zero, li, hh);
-    acc_rows_to_lds<D>(vt, dvacc, 1.0f, zero, li, hh);
+    E* kt = ((wave >> 1) ? so0 : sq0) + (wave & 1) * 32 * D;
+    E* vt = ((wave >> 1) ? so1 : sq1) + (wave & 1) * 32 * D;
+    acc_rows_to_lds<D, E>(kt, dkacc, p.scale, zero, li, hh);
+    acc_rows_to_lds<D, E>(vt, dvacc, 1.0f, zero, li, hh);
     const int row0 = kb + 32 * wave;
-    lds_rows_to_global<D>(kt, p.dk + head_off + (size_t)row0 * D, N - row0, lane);
-    lds_rows_to_global<D>(vt, p.dv + head_off + (size_t)row0 * D, N - row0, lane);
+    lds_rows_to_global_strided<D, E>(kt, dkg + (int64_t)row0 * p.sdk.n, p.sdk.n, N - row0, lane);
+    lds_rows_to_global_strided<D, E>(vt, dvg + (int64_t)row0 * p.sdv.n, p.sdv.n, N - row0, lane);
   }
   prefetched = !DROPOUT && has_next;
   }  // block
@@ -615,17 +640,20 @@ struct QCfg {
   static_assert(LOADS * THREADS == BN * CHUNKS, "tile/thread mismatch");
 };
 
-template <int D, bool CAUSAL, bool DROPOUT>
+template <typename E, int D, bool CAUSAL, bool DROPOUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
   using C = QCfg<D>;
+  using V8 = typename Elem<E>::v8;
+  using V4 = typename Elem<E>::v4;
+  constexpr int ES = 2;
   constexpr int BN = C::BN, NW = C::NW, TILE = C::TILE;
   constexpr int KC = D / 16;
   constexpr int DU = D / 32;
-  __shared__ __attribute__((aligned(1024))) bf16 sk0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sk1[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sv0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sv1[TILE];
+  __shared__ __attribute__((aligned(1024))) E sk0[TILE];
+  __shared__ __attribute__((aligned(1024))) E sk1[TILE];
+  __shared__ __attribute__((aligned(1024))) E sv0[TILE];
+  __shared__ __attribute__((aligned(1024))) E sv1[TILE];
 
   const int N = p.N;
   const int nqb = p.num_blocks;
@@ -654,38 +682,51 @@ void bwd_dq_kernel(BwdParams p) {
   if (CAUSAL) nfree = min(nfree, q0 / BN);
   nfree = min(nfree, nkb);
 
-  const size_t head_off = (size_t)head * N * D;
+  // (b, h) slices through per-tensor strides
+  const E* qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h);
+  const E* kg = (const E*)p.k + (bi * p.sk.b + hi * p.sk.h);
+  const E* vg = (const E*)p.v + (bi * p.sv.b + hi * p.sv.h);
+  const E* dog = (const E*)p.dout + (bi * p.sdo.b + hi * p.sdo.h);
+  const E* og = (const E*)p.o + (bi * p.so.b + hi * p.so.h);
+  E* dqg = (E*)p.dq + (bi * p.sdq.b + hi * p.sdq.h);
+  const int sqn = (int)p.sq.n, skn = (int)p.sk.n, svn = (int)p.sv.n, son_ = (int)p.sdo.n;
   // Q^T and dO^T as B operands (k = head dimension): lane holds row qi,
   // elements 16c + 8hh .. +7, read from LDS after the block's rows have been
   // copied in (below).
-  bf16x8 qreg[KC], oreg[KC];
+  V8 qreg[KC], oreg[KC];
 
   // The copies cover the tiles [0, nkb) only: copies past them (issued without
   // a branch) read zeros without touching memory.
-  const uint32_t kv_bytes = (uint32_t)min(nkb * BN, N) * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, kv_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, kv_bytes);
-  // Byte offset of this lane's i-th 16-byte copy within a tile: chunk slot
-  // (i * NW + wave) * 64 + lane, i.e. row (i * NW + wave) * 64 / CHUNKS +
-  // lane / CHUNKS, chunk lane % CHUNKS.  The swizzle depends on the row mod 16,
-  // which does not change with i, so copy i is copy 0 moved by i * NW * 64
-  // chunks.
-  static_assert((NW * 64 / C::CHUNKS) % 16 == 0, "copy rows must keep their swizzle");
-  uint32_t ld_off0;
+  const int krows = min(nkb * BN, N);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, rows_bytes(krows, skn, D, ES));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, rows_bytes(krows, svn, D, ES));
+  // Copy i of this lane fills chunk slot (i * NW + wave) * 64 + lane, i.e.
+  // row i * COPY_ROWS + wave * 64 / CHUNKS + lane / CHUNKS, chunk
+  // lane % CHUNKS.  The swizzle depends on the row mod 16, which does not
+  // change with i, so copy i is copy 0 moved by i * COPY_ROWS rows.  Per
+  // tensor, the lane's part of the byte offset is ldl_*; the rest is
+  // wave-uniform and is added to it.
+  constexpr int COPY_ROWS = NW * 64 / C::CHUNKS;
+  static_assert(COPY_ROWS % 16 == 0, "copy rows must keep their swizzle");
+  const int wrow = wave * 64 / C::CHUNKS;
+  uint32_t ldl_k, ldl_v;
+  int crow, lch;  // this lane's row within a copy round and its chunk's element offset
   {
-    const int r = wave * 64 / C::CHUNKS + lane / C::CHUNKS, pc = lane % C::CHUNKS;
-    ld_off0 = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
+    const int r = wrow + lane / C::CHUNKS, pc = lane % C::CHUNKS;
+    crow = lane / C::CHUNKS;
+    lch = (pc ^ swz<D>(r)) * 8;
+    ldl_k = (uint32_t)(crow * skn + lch) * ES;
+    ldl_v = (uint32_t)(crow * svn + lch) * ES;
   }
-  auto ld_off = [&](int i) { return ld_off0 + (uint32_t)(i * NW * 64 * 16); };
   // Copy piece x of tile jt (x < LOADS: K, else V) into stage S.
   auto issue_piece = [&](int jt, auto par_t, int x) {
     constexpr int S = decltype(par_t)::value;
-    const uint32_t base = (uint32_t)jt * (BN * D * 2);
     const int i = x % C::LOADS;
+    const int row0 = jt * BN + i * COPY_ROWS + wrow;  // wave-uniform
     if (x < C::LOADS)
-      lds_dma16(krs, (S ? sk1 : sk0) + (i * NW + wave) * 512, ld_off(i) + base);
+      lds_dma16_row(krs, (S ? sk1 : sk0) + (i * NW + wave) * 512, ldl_k, row0, (uint32_t)skn * ES);
     else
-      lds_dma16(vrs, (S ? sv1 : sv0) + (i * NW + wave) * 512, ld_off(i) + base);
+      lds_dma16_row(vrs, (S ? sv1 : sv0) + (i * NW + wave) * 512, ldl_v, row0, (uint32_t)svn * ES);
   };
   auto issue = [&](int jt, auto par_t) {
 #pragma unroll
@@ -704,24 +745,26 @@ void bwd_dq_kernel(BwdParams p) {
     // past N read as zero); every wave then reads its rows into registers.
     // Loading them straight into registers, a lane per row, cost more than
     // this whole round trip.  The stages are free again after the barrier.
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q + head_off, (uint32_t)N * D * 2);
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.dout + head_off, (uint32_t)N * D * 2);
-    const uint32_t qt0 = (uint32_t)(q0 / BN) * (BN * D * 2);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qg, rows_bytes(N, sqn, D, ES));
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(dog, rows_bytes(N, son_, D, ES));
+    const uint32_t ldl_q = (uint32_t)(crow * sqn + lch) * ES;
+    const uint32_t ldl_o = (uint32_t)(crow * son_ + lch) * ES;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      lds_dma16(qrs, sk0 + (i * NW + wave) * 512, ld_off(i) + qt0);
-      lds_dma16(qrs, sk1 + (i * NW + wave) * 512, ld_off(i) + qt0 + (uint32_t)(BN * D * 2));
-      lds_dma16(ors, sv0 + (i * NW + wave) * 512, ld_off(i) + qt0);
-      lds_dma16(ors, sv1 + (i * NW + wave) * 512, ld_off(i) + qt0 + (uint32_t)(BN * D * 2));
+      const int row0 = q0 + i * COPY_ROWS + wrow;  // wave-uniform
+      lds_dma16_row(qrs, sk0 + (i * NW + wave) * 512, ldl_q, row0, (uint32_t)sqn * ES);
+      lds_dma16_row(qrs, sk1 + (i * NW + wave) * 512, ldl_q, row0 + BN, (uint32_t)sqn * ES);
+      lds_dma16_row(ors, sv0 + (i * NW + wave) * 512, ldl_o, row0, (uint32_t)son_ * ES);
+      lds_dma16_row(ors, sv1 + (i * NW + wave) * 512, ldl_o, row0 + BN, (uint32_t)son_ * ES);
     }
     wait_vmem();
     __syncthreads();
-    const bf16* qt = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
-    const bf16* ot = ((wave >> 1) ? sv1 : sv0) + (wave & 1) * 32 * D;
+    const E* qt = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
+    const E* ot = ((wave >> 1) ? sv1 : sv0) + (wave & 1) * 32 * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      qreg[c] = *(const bf16x8*)(qt + roff[c]);
-      oreg[c] = *(const bf16x8*)(ot + roff[c]);
+      qreg[c] = *(const V8*)(qt + roff[c]);
+      oreg[c] = *(const V8*)(ot + roff[c]);
     }
     __syncthreads();  // every wave has its rows before the first K/V tile lands there
   }
@@ -731,9 +774,9 @@ void bwd_dq_kernel(BwdParams p) {
   // Both go to the workspace, where the dK/dV stage reads them.
   float drow = 0.0f, lrow = INFINITY;
   if (qi < N) {
-    const bf16* orow = p.o + head_off + (size_t)qi * D + 8 * hh;
+    const E* orow = og + (int64_t)qi * p.so.n + 8 * hh;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) drow = dot8(*(const bf16x8*)(orow + 16 * c), oreg[c], drow);
+    for (int c = 0; c < KC; ++c) drow = Elem<E>::dot8(*(const V8*)(orow + 16 * c), oreg[c], drow);
     const float lv = p.lse[(size_t)head * N + qi];
     lrow = lv == -INFINITY ? INFINITY : lv * kLog2e;
   }
@@ -764,18 +807,18 @@ void bwd_dq_kernel(BwdParams p) {
   auto step = [&](int j, auto par_t, auto masked_t) {
     constexpr int S = decltype(par_t)::value;  // j & 1
     constexpr bool MASKED = decltype(masked_t)::value;
-    const bf16* ks = S ? sk1 : sk0;
-    const bf16* vs = S ? sv1 : sv0;
+    const E* ks = S ? sk1 : sk0;
+    const E* vs = S ? sv1 : sv0;
     __syncthreads();  // tile j resident; every wave is done with tile j-1
 
     // ---- S^T = K Q^T and dP^T = V dO^T: key tile t (32 keys), k-step c.
     f32x16 sacc[2], pacc[2];
     const f32x16 zero = {};
     constexpr int NS = 4 * KC;
-    bf16x8 ring[3];
+    V8 ring[3];
     auto sread = [&](int i) {
       const int m = i / KC, c = i % KC;
-      return *(const bf16x8*)((m < 2 ? ks : vs) + roff[c] + (m & 1) * 32 * D);
+      return *(const V8*)((m < 2 ? ks : vs) + roff[c] + (m & 1) * 32 * D);
     };
     // Priority while this wave's exponentials and dS are on the critical
     // path: the other workgroup's wave on the SIMD, in its dQ products,
@@ -784,7 +827,7 @@ void bwd_dq_kernel(BwdParams p) {
     ring[0] = sread(0);
     ring[1] = sread(1);
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 dsb[4];  // dS^T as B operands: chunk cc holds keys 16cc + 8(x/4) + 4hh + x%4
+    V8 dsb[4];  // dS^T as B operands: chunk cc holds keys 16cc + 8(x/4) + 4hh + x%4
     // P^T of key tile t, keys 32t + 8g + 4hh + e of the tile, in place.
     auto p_elems = [&](int t, int g) {
 #pragma unroll
@@ -804,7 +847,7 @@ void bwd_dq_kernel(BwdParams p) {
         const int r = 4 * g + e;
         float dp = pacc[t][r];
         if constexpr (DROPOUT) dp *= dropout_z(p, qi, j * BN + 32 * t + 8 * g + 4 * hh + e, hi, bi);
-        dsb[2 * t + (g >> 1)][4 * (g & 1) + e] = (bf16)(sacc[t][r] * (dp - drow));
+        dsb[2 * t + (g >> 1)][4 * (g & 1) + e] = (E)(sacc[t][r] * (dp - drow));
       }
     };
 #pragma unroll
@@ -817,7 +860,7 @@ void bwd_dq_kernel(BwdParams p) {
       if (i + 2 < NS) ring[(i + 2) % 3] = sread(i + 2);
       const int m = i / KC, c = i % KC;
       f32x16& acc = m < 2 ? sacc[m & 1] : pacc[m & 1];
-      acc = mfma32(ring[i % 3], m < 2 ? qreg[c] : oreg[c], c == 0 ? zero : acc);
+      acc = Elem<E>::mma(ring[i % 3], m < 2 ? qreg[c] : oreg[c], c == 0 ? zero : acc);
       if ((c * 4) % KC == 0) {
         const int g = c * 4 / KC;
         if (m == 1) p_elems(0, g);
@@ -829,13 +872,13 @@ void bwd_dq_kernel(BwdParams p) {
 
     // ---- dQ^T += K^T dS^T (contraction over the 64 keys)
     __builtin_amdgcn_s_setprio(0);
-    const lds_bf16* kt = to_lds(ks);
+    const lds_bf16* kt = (const lds_bf16*)ks;
     constexpr int NQ = 4 * DU;  // index = (cc, u)
     auto tnext = [&](int i) {
       const int cc = i / DU, u = i % DU;
-      const bf16x4 lo = lds_read_tr4(kt + toff[0][u] + 16 * cc * D);
-      const bf16x4 h4 = lds_read_tr4(kt + toff[1][u] + 16 * cc * D);
-      return bf16x8{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
+      const V4 lo = __builtin_bit_cast(V4, lds_read_tr4(kt + toff[0][u] + 16 * cc * D));
+      const V4 h4 = __builtin_bit_cast(V4, lds_read_tr4(kt + toff[1][u] + 16 * cc * D));
+      return V8{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
     };
     ring[0] = tnext(0);
     ring[1] = tnext(1);
@@ -844,7 +887,7 @@ void bwd_dq_kernel(BwdParams p) {
     for (int i = 0; i < NQ; ++i) {
       if (i + 2 < NQ) ring[(i + 2) % 3] = tnext(i + 2);
       const int cc = i / DU, u = i % DU;
-      qacc[u] = mfma32(ring[i % 3], dsb[cc], qacc[u]);
+      qacc[u] = Elem<E>::mma(ring[i % 3], dsb[cc], qacc[u]);
       // chunks 2, 3 (key tile 1) are first used by MFMA 2*DU
       if (i < 4) ds_elems(1, i);
       __builtin_amdgcn_sched_barrier(0);
@@ -877,48 +920,49 @@ void bwd_dq_kernel(BwdParams p) {
   __syncthreads();
   {
     const int qw = q0 + wave * 32;
-    bf16* qt = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
-    acc_rows_to_lds<D>(qt, qacc, p.scale, false, li, hh);
-    lds_rows_to_global<D>(qt, p.dq + head_off + (size_t)qw * D, N - qw, lane);
+    E* qt = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
+    acc_rows_to_lds<D, E>(qt, qacc, p.scale, false, li, hh);
+    lds_rows_to_global_strided<D, E>(qt, dqg + (int64_t)qw * p.sdq.n, p.sdq.n, N - qw, lane);
   }
   }  // item
 }
 
 // D_i = sum_k dO_ik O_ik and LSE_i * log2(e) (+inf for an empty row, so that
 // the recomputed probabilities exp2(s - LSE*log2e) vanish).  D/8 lanes per row.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o,
-                                                      const bf16* __restrict__ dout,
-                                                      const float* __restrict__ lse,
-                                                      float* __restrict__ delta,
-                                                      float* __restrict__ lse2, int64_t rows) {
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t rows) {
+  typedef E v8 __attribute__((ext_vector_type(8)));
   constexpr int LPR = D / 8;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = t / LPR;
   const int ch = (int)(t % LPR);
   float s = 0.0f;
   if (row < rows) {
-    const bf16x8 ov = *(const bf16x8*)(o + row * D + ch * 8);
-    const bf16x8 dv = *(const bf16x8*)(dout + row * D + ch * 8);
+    const int head = (int)(row / p.N), n = (int)(row - (int64_t)head * p.N);
+    const int bi = head / p.H, hi = head - bi * p.H;
+    const v8 ov = *(const v8*)((const E*)p.o + (bi * p.so.b + hi * p.so.h + (int64_t)n * p.so.n) +
+                               ch * 8);
+    const v8 dv = *(const v8*)((const E*)p.dout +
+                               (bi * p.sdo.b + hi * p.sdo.h + (int64_t)n * p.sdo.n) + ch * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = fmaf((float)ov[e], (float)dv[e], s);
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, LPR);
   if (row < rows && ch == 0) {
-    delta[row] = s;
-    const float lv = lse[row];
-    lse2[row] = lv == -INFINITY ? INFINITY : lv * kLog2e;
+    p.delta[row] = s;
+    const float lv = p.lse[row];
+    p.lse2[row] = lv == -INFINITY ? INFINITY : lv * kLog2e;
   }
 }
 
-template <int D, bool CAUSAL, bool DROPOUT>
+template <typename E, int D, bool CAUSAL, bool DROPOUT>
 hipError_t launch_main(BwdParams p, int heads, int stages, hipStream_t s) {
   // dQ first: it writes the per-row terms the dK/dV kernel reads.
   if (stages & kBwdQ) {
     p.num_blocks = (p.N + QCfg<D>::BM - 1) / QCfg<D>::BM;
     const int per_head = CAUSAL ? (p.num_blocks + 1) / 2 : p.num_blocks;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROPOUT>), dim3(heads * per_head),
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, DROPOUT>), dim3(heads * per_head),
                        dim3(QCfg<D>::THREADS), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -935,47 +979,55 @@ hipError_t launch_main(BwdParams p, int heads, int stages, hipStream_t s) {
         cus <= 0)
       cus = 256;
     const int grid = p.units < cus ? p.units : cus;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROPOUT>), dim3(grid), dim3(KvCfg<D>::THREADS), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, DROPOUT>), dim3(grid), dim3(KvCfg<D>::THREADS), 0,
                        s, p);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
-template <int D>
+template <typename E, int D>
 hipError_t run(const BwdArgs& a, const BwdParams& p, int stages, hipStream_t s) {
   if (stages & kBwdPre) {
     const int64_t rows = (int64_t)a.B * a.H * a.N;
     const int64_t pre_threads = rows * (D / 8);
-    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0,
-                       s, (const bf16*)a.o, (const bf16*)a.dout, a.lse, a.delta, a.lse2, rows);
+    hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((unsigned)((pre_threads + 255) / 256)),
+                       dim3(256), 0, s, p, rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int heads = a.B * a.H;
   const bool drop = a.dropout_p > 0.0f;
   if (a.causal)
-    return drop ? launch_main<D, true, true>(p, heads, stages, s)
-                : launch_main<D, true, false>(p, heads, stages, s);
-  return drop ? launch_main<D, false, true>(p, heads, stages, s)
-              : launch_main<D, false, false>(p, heads, stages, s);
+    return drop ? launch_main<E, D, true, true>(p, heads, stages, s)
+                : launch_main<E, D, true, false>(p, heads, stages, s);
+  return drop ? launch_main<E, D, false, true>(p, heads, stages, s)
+              : launch_main<E, D, false, false>(p, heads, stages, s);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
+hipError_t launch_bwd_16(const BwdArgs& a, int stages, hipStream_t s) {
   BwdParams p;
-  p.q = (const bf16*)a.q;
-  p.k = (const bf16*)a.k;
-  p.v = (const bf16*)a.v;
-  p.dout = (const bf16*)a.dout;
-  p.o = (const bf16*)a.o;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.dout = a.dout;
+  p.o = a.o;
+  p.sq = a.sq;
+  p.sk = a.sk;
+  p.sv = a.sv;
+  p.so = a.so;
+  p.sdo = a.sdo;
+  p.sdq = a.sdq;
+  p.sdk = a.sdk;
+  p.sdv = a.sdv;
   p.lse = a.lse;
   p.lse2 = a.lse2;
   p.delta = a.delta;
-  p.dq = (bf16*)a.dq;
-  p.dk = (bf16*)a.dk;
-  p.dv = (bf16*)a.dv;
+  p.dq = a.dq;
+  p.dk = a.dk;
+  p.dv = a.dv;
   p.key_lens = a.key_lens;
   p.H = a.H;
   p.N = a.N;
@@ -986,7 +1038,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
   p.drop_scale = a.drop_scale;
   p.seed_lo = (uint32_t)(a.seed & 0xffffffffu);
   p.seed_hi = (uint32_t)(a.seed >> 32);
-  return a.d == 64 ? run<64>(a, p, stages, s) : run<128>(a, p, stages, s);
+  if (a.fp16) return a.d == 64 ? run<f16, 64>(a, p, stages, s) : run<f16, 128>(a, p, stages, s);
+  return a.d == 64 ? run<bf16, 64>(a, p, stages, s) : run<bf16, 128>(a, p, stages, s);
 }
 
 }  // namespace fa

@@ -16,6 +16,10 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -50,6 +54,19 @@ __device__ __forceinline__ void keep(const bf16x8& x) { asm volatile("" ::"v"(x)
 // Wait states covering the latency of the last mfma32_acc before its
 // accumulator is read.
 __device__ __forceinline__ void acc_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+// The same wait states, tied to the accumulators they protect: the asm claims
+// to rewrite x, so every later read of x (a VALU read of the MFMA results)
+// is ordered after the wait, and the MFMAs that produced x before it.  Tie
+// further accumulators with tie_acc/tie_vacc right after (inline asm
+// statements with side effects keep their order).
+__device__ __forceinline__ void settle_acc(f32x16& x) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x));
+}
+__device__ __forceinline__ void settle_vacc(f32x16& x) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
+}
+__device__ __forceinline__ void tie_acc(f32x16& x) { asm volatile("" : "+a"(x)); }
+__device__ __forceinline__ void tie_vacc(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 // LDS transposing read of four 16-bit elements.  Within each group of 16 lanes,
 // lane t receives element (t % 4) of the 8-byte load issued by lane 4*e + t/4 as
@@ -141,6 +158,14 @@ __device__ __forceinline__ u32x4 philox(uint32_t c0, uint32_t c1, uint32_t c2, u
   return out;
 }
 
+// Word i & 3 of a Philox output, where i may differ from lane to lane.  A
+// dynamic vector extract lowers to selects.  A chain of comparisons against i
+// is instead turned into a switch, that is, branches that diverge across the
+// lanes, and the register allocator has been seen to place a whole-wave
+// register copy inside one arm of such a branch, leaving it unwritten in the
+// lanes that skipped that arm.
+__device__ __forceinline__ uint32_t philox_word(const u32x4& w, int i) { return w[i & 3]; }
+
 // XOR swizzle of the 16-byte chunks of a row-major bf16 tile with D-element
 // rows: the physical chunk slot of logical chunk c in tile row r is c ^ swz(r).
 // d = 128 (16 chunks, 256-byte rows): 16 consecutive rows get 16 distinct
@@ -157,13 +182,84 @@ __device__ __forceinline__ int swz(int r) {
   }
 }
 
+// Element types of the 16-bit paths and their MFMA: D(32x32, f32) += A B with
+// A 32x16 and B 16x32 of that type (same lane layout as mfma32).
+template <typename E>
+struct Elem;
+template <>
+struct Elem<bf16> {
+  typedef bf16x8 v8;
+  typedef bf16x4 v4;
+  static __device__ __forceinline__ f32x16 mma(const v8& a, const v8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // acc += A B (acc = A B) with acc pinned to AccVGPRs (see mfma32_acc)
+  static __device__ __forceinline__ void mma_acc(f32x16& acc, const v8& a, const v8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void mma_acc_first(f32x16& acc, const v8& a, const v8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  }
+  // d = A B and d += A B with B read from AccVGPRs and d in ordinary VGPRs.
+  // The compiler does not know these are MFMAs: a VALU read of d must follow
+  // acc_settle() after the last of them.
+  static __device__ __forceinline__ void mma_b_acc_first(f32x16& d, const v8& a, const v8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  }
+  static __device__ __forceinline__ void mma_b_acc(f32x16& d, const v8& a, const v8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+  }
+  // acc + sum_e a[e] * b[e] over eight pairs (exact products, fp32 sums)
+  static __device__ __forceinline__ float dot8(const v8& a, const v8& b, float acc) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a[e], a[e + 1]}, bf16x2{b[e], b[e + 1]}, acc,
+                                            false);
+    return acc;
+  }
+};
+template <>
+struct Elem<f16> {
+  typedef f16x8 v8;
+  typedef f16x4 v4;
+  static __device__ __forceinline__ f32x16 mma(const v8& a, const v8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void mma_acc(f32x16& acc, const v8& a, const v8& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void mma_acc_first(f32x16& acc, const v8& a, const v8& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void mma_b_acc_first(f32x16& d, const v8& a, const v8& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  }
+  static __device__ __forceinline__ void mma_b_acc(f32x16& d, const v8& a, const v8& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+  }
+  static __device__ __forceinline__ float dot8(const v8& a, const v8& b, float acc) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      acc = __builtin_amdgcn_fdot2(f16x2{a[e], a[e + 1]}, f16x2{b[e], b[e + 1]}, acc, false);
+    return acc;
+  }
+};
+
+// Bytes a buffer resource must span to cover rows [0, rows) of D elements
+// each, `sn` elements apart (sn >= D): reads of any row >= rows then fall
+// outside it and return zeros.
+__device__ __forceinline__ uint32_t rows_bytes(int rows, int64_t sn, int D, int esize) {
+  return rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * sn + D) * esize);
+}
+
 // Write a wave's 32 x D fp32 accumulator tile, held in the MFMA output layout
 // with one row per lane (lane li: row li; acc[u][r]: column 32u + 8(r/4) +
 // 4hh + r%4), as bf16 (acc * mul, or zeros) into a row-major 32 x D LDS tile
 // whose 16-byte chunks are XOR-swizzled by swz<D>(row).
-template <int D>
-__device__ __forceinline__ void acc_rows_to_lds(bf16* tile, const f32x16 (&acc)[D / 32], float mul,
+template <int D, typename E = bf16>
+__device__ __forceinline__ void acc_rows_to_lds(E* tile, const f32x16 (&acc)[D / 32], float mul,
                                                 bool zero, int li, int hh) {
+  typedef E v4 __attribute__((ext_vector_type(4)));
   // Opaque lane indices: the addresses are computed here, where they are
   // used, rather than hoisted out of the caller's loop and kept live.
   asm volatile("" : "+v"(li), "+v"(hh));
@@ -171,10 +267,10 @@ __device__ __forceinline__ void acc_rows_to_lds(bf16* tile, const f32x16 (&acc)[
   for (int u = 0; u < D / 32; ++u)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      bf16x4 v;
+      v4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = zero ? (bf16)0.0f : (bf16)(acc[u][4 * g + e] * mul);
-      *(bf16x4*)(tile + li * D + (((4 * u + g) ^ swz<D>(li)) * 8) + 4 * hh) = v;
+      for (int e = 0; e < 4; ++e) v[e] = zero ? (E)0.0f : (E)(acc[u][4 * g + e] * mul);
+      *(v4*)(tile + li * D + (((4 * u + g) ^ swz<D>(li)) * 8) + 4 * hh) = v;
     }
 }
 
@@ -191,6 +287,22 @@ __device__ __forceinline__ void lds_rows_to_global(const bf16* tile, bf16* dst, 
     const int r = i * RPI + lane / CH;
     const bf16x8 v = *(const bf16x8*)(tile + r * D + ((c ^ swz<D>(r)) * 8));
     if (r < nrows) *(bf16x8*)(dst + (size_t)r * D + c * 8) = v;
+  }
+}
+
+// The same copy to rows `sn` elements apart (rows [0, min(nrows, 32))).
+template <int D, typename E>
+__device__ __forceinline__ void lds_rows_to_global_strided(const E* tile, E* dst, int64_t sn,
+                                                           int nrows, int lane) {
+  constexpr int CH = D / 8, RPI = 64 / CH;
+  typedef E v8 __attribute__((ext_vector_type(8)));
+  asm volatile("" : "+v"(lane));  // see acc_rows_to_lds
+  const int c = lane % CH;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CH;
+    const v8 v = *(const v8*)(tile + r * D + ((c ^ swz<D>(r)) * 8));
+    if (r < nrows) *(v8*)(dst + (int64_t)r * sn + c * 8) = v;
   }
 }
 
@@ -221,6 +333,37 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, const void* 
                                           uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, voff, 0, 0, 0);
 }
+
+// The same for the wave-uniform tile row `row0` of a tensor whose rows are
+// `row_bytes` apart: lane data from byte row0 * row_bytes + voff.  The row
+// offset goes into the per-lane offset, not the instruction's scalar-offset
+// field: the buffer range check that turns reads past the last row into
+// zeros looks at the per-lane offset (plus the immediate) only, so a row
+// offset in the scalar field would let tiles past the end read whatever
+// memory follows the slice.  row0 is made opaque (kept in a scalar register)
+// so that the product is formed at the copy, not hoisted out of the loop as
+// one register per copy.
+__device__ __forceinline__ void lds_dma16_row(__amdgpu_buffer_rsrc_t r, const void* lds_wave_base,
+                                              uint32_t voff, int row0, uint32_t row_bytes) {
+  asm volatile("" : "+s"(row0));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16,
+                                           voff + (uint32_t)row0 * row_bytes, 0, 0, 0);
+}
+
+// Marks x as still in use at this point (see keep).
+template <typename T>
+__device__ __forceinline__ void keep_v(const T& x) {
+  asm volatile("" ::"v"(x));
+}
+template <typename T>
+__device__ __forceinline__ void pin_v(T& x) {
+  asm volatile("" : "+v"(x));
+}
+// An opaque redefinition of a per-lane offset: address arithmetic built on it
+// is formed after this point, where it is used, instead of being hoisted out
+// of the loop as one register per combination of offset and constant.
+__device__ __forceinline__ void opaque(int& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void opaque_u(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
 // Wait until this wave's outstanding vector-memory loads (including LDS DMA)
 // have completed.

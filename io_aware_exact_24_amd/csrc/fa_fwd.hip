@@ -38,13 +38,15 @@ namespace fa {
 namespace {
 
 struct FwdParams {
-  const bf16* q;
-  const bf16* k;
-  const bf16* v;
-  bf16* o;
-  float* lse;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // contiguous [B, H, N]
   const int32_t* key_lens;
+  Strides sq, sk, sv, so;  // element strides (batch, head, row); d is contiguous
   int H, N, num_qblocks;
+  int causal;  // fp32 kernel only (the 16-bit kernel takes it as a template argument)
   float scale_log2;  // scale * log2(e): scores enter exp2 in these units
   uint32_t drop_threshold;
   float drop_scale;
@@ -66,25 +68,29 @@ struct FwdCfg {
   static constexpr int CHUNKS = D / 8;          // 16-byte chunks per row
   static constexpr int TILE = BN * D;           // elements per K or V tile
   static constexpr int LOADS = BN * CHUNKS / THREADS;  // 16-byte copies per thread per tile
+  static constexpr int COPY_ROWS = THREADS / CHUNKS;   // tile rows one copy round covers
   static_assert(LOADS * THREADS == BN * CHUNKS, "tile/thread mismatch");
 };
 
-template <int D, bool CAUSAL, bool DROPOUT, bool SPLIT>
+template <typename E, int D, bool CAUSAL, bool DROPOUT, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
-void fwd_bf16_kernel(FwdParams p) {
+void fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
+  using V8 = typename Elem<E>::v8;
+  using V4 = typename Elem<E>::v4;
+  constexpr int ES = 2;  // bytes per element
   constexpr int BN = C::BN, NW = C::NW, TILE = C::TILE;
   constexpr int KC = D / 16;  // MFMA k-steps over the head dimension
   constexpr int DU = D / 32;  // 32-wide blocks of the head dimension
   // K and V tiles, two stages each.  Separate objects let the compiler see
   // that a copy into one stage cannot alias reads of another, so it does not
   // make those reads wait for the copy.
-  __shared__ __attribute__((aligned(1024))) bf16 sk0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sk1[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sv0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sv1[TILE];
-  auto kbuf = [&](int stage) -> bf16* { return stage ? sk1 : sk0; };
-  auto vbuf = [&](int stage) -> bf16* { return stage ? sv1 : sv0; };
+  __shared__ __attribute__((aligned(1024))) E sk0[TILE];
+  __shared__ __attribute__((aligned(1024))) E sk1[TILE];
+  __shared__ __attribute__((aligned(1024))) E sv0[TILE];
+  __shared__ __attribute__((aligned(1024))) E sv1[TILE];
+  auto kbuf = [&](int stage) -> E* { return stage ? sk1 : sk0; };
+  auto vbuf = [&](int stage) -> E* { return stage ? sv1 : sv0; };
 
   const int N = p.N;
   const int nqb = p.num_qblocks;
@@ -129,43 +135,51 @@ void fwd_bf16_kernel(FwdParams p) {
     nfree = min(max(nfree - jt0, 0), nkb);
   }
 
-  const size_t head_off = (size_t)head * N * D;
-  const bf16* __restrict__ qg = p.q + head_off;
+  // (b, h) slices through per-tensor strides; rows are p.s?.n elements apart.
+  const E* __restrict__ qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h);
+  const E* kg = (const E*)p.k + (bi * p.sk.b + hi * p.sk.h);
+  const E* vg = (const E*)p.v + (bi * p.sv.b + hi * p.sv.h);
+  E* og = (E*)p.o + (bi * p.so.b + hi * p.so.h);
+  const int skn = (int)p.sk.n, svn = (int)p.sv.n;
   // The copies cover the tiles [0, nkb) only: copies past them (issued without
   // a branch) read zeros without touching memory.
-  const uint32_t kv_bytes = (uint32_t)min((jt0 + nkb) * BN, N) * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head_off, kv_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head_off, kv_bytes);
+  const int krows = min((jt0 + nkb) * BN, N);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, rows_bytes(krows, skn, D, ES));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, rows_bytes(krows, svn, D, ES));
 
   // Q^T as the B operand of S^T = K Q^T: lane holds Q[qi][16c + 8hh .. +7].
-  bf16x8 qreg[KC];
+  V8 qreg[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     if (qi < N) {
-      qreg[c] = *(const bf16x8*)(qg + (size_t)qi * D + 16 * c + 8 * hh);
+      qreg[c] = *(const V8*)(qg + (int64_t)qi * p.sq.n + 16 * c + 8 * hh);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qreg[c][e] = (bf16)0.0f;
+      for (int e = 0; e < 8; ++e) qreg[c][e] = (E)0.0f;
     }
   }
 
   // Byte offset of this lane's i-th 16-byte copy within a tile: chunk slot
-  // (i * NW + wave) * 64 + lane, i.e. row (i * NW + wave) * 64 / CHUNKS +
-  // lane / CHUNKS, chunk lane % CHUNKS.  The swizzle depends on the row mod 16,
-  // which does not change with i, so copy i is copy 0 moved by i * NW * 64
-  // chunks.
-  static_assert((NW * 64 / C::CHUNKS) % 16 == 0, "copy rows must keep their swizzle");
-  uint32_t ld_off0;
+  // (i * NW + wave) * 64 + lane, i.e. row i * COPY_ROWS + r0 with
+  // r0 = wave * 64 / CHUNKS + lane / CHUNKS, chunk lane % CHUNKS.  The swizzle
+  // depends on the row mod 16, which does not change with i, so copy i is
+  // copy 0 moved by i * COPY_ROWS rows: a wave-uniform offset, added with
+  // the tile's to the lane's part.
+  static_assert(C::COPY_ROWS % 16 == 0, "copy rows must keep their swizzle");
+  uint32_t kld0, vld0;
   {
     const int r = wave * 64 / C::CHUNKS + lane / C::CHUNKS, pc = lane % C::CHUNKS;
-    ld_off0 = (uint32_t)(r * D + ((pc ^ swz<D>(r)) * 8)) * 2;
+    const int lch = (pc ^ swz<D>(r)) * 8;
+    kld0 = (uint32_t)(r * skn + lch) * ES;
+    vld0 = (uint32_t)(r * svn + lch) * ES;
   }
-  auto ld_off = [&](int i) { return ld_off0 + (uint32_t)(i * NW * 64 * 16); };
   auto issue_k_piece = [&](int jt, int stage, int i) {
-    lds_dma16(krs, kbuf(stage) + (i * NW + wave) * 512, ld_off(i) + (uint32_t)(jt0 + jt) * (BN * D * 2));
+    lds_dma16_row(krs, kbuf(stage) + (i * NW + wave) * 512, kld0, (jt0 + jt) * BN + i * C::COPY_ROWS,
+                  (uint32_t)skn * ES);
   };
   auto issue_v_piece = [&](int jt, int stage, int i) {
-    lds_dma16(vrs, vbuf(stage) + (i * NW + wave) * 512, ld_off(i) + (uint32_t)(jt0 + jt) * (BN * D * 2));
+    lds_dma16_row(vrs, vbuf(stage) + (i * NW + wave) * 512, vld0, (jt0 + jt) * BN + i * C::COPY_ROWS,
+                  (uint32_t)svn * ES);
   };
   auto issue_k = [&](int jt, int stage) {
 #pragma unroll
@@ -205,15 +219,15 @@ void fwd_bf16_kernel(FwdParams p) {
   float l = 0.0f;          // this lane's partial row sum (its 16 keys of every 32)
 
   auto qk = [&](int stage, f32x16 (&s)[2]) {
-    const bf16* ks = kbuf(stage);
+    const E* ks = kbuf(stage);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const bf16x8 a = *(const bf16x8*)(ks + koff[c] + t * 32 * D);
-        s[t] = mfma32(a, qreg[c], s[t]);
+        const V8 a = *(const V8*)(ks + koff[c] + t * 32 * D);
+        s[t] = Elem<E>::mma(a, qreg[c], s[t]);
       }
     }
   };
@@ -301,11 +315,11 @@ void fwd_bf16_kernel(FwdParams p) {
     // Priority while this wave's exponentials are on the critical path: the
     // other wave on the SIMD (in phase B, MFMA-bound) fills the gaps.
     __builtin_amdgcn_s_setprio(3);
-    const bf16* ks = kbuf(PAR ^ 1);
-    auto kread = [&](int i) { return *(const bf16x8*)(ks + koff[i % KC] + (i / KC) * 32 * D); };
-    bf16x8 pb[4];
+    const E* ks = kbuf(PAR ^ 1);
+    auto kread = [&](int i) { return *(const V8*)(ks + koff[i % KC] + (i / KC) * 32 * D); };
+    V8 pb[4];
     float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    bf16x8 ka[3];
+    V8 ka[3];
     if constexpr (HAS_NEXT) {
       ka[0] = kread(0);
       ka[1] = kread(1);
@@ -327,7 +341,7 @@ void fwd_bf16_kernel(FwdParams p) {
       if constexpr (HAS_NEXT) {
         if (i + 2 < NA) ka[(i + 2) % 3] = kread(i + 2);
         const f32x16 zero = {};
-        sn[t] = mfma32(ka[i % 3], qreg[c], c == 0 ? zero : sn[t]);
+        sn[t] = Elem<E>::mma(ka[i % 3], qreg[c], c == 0 ? zero : sn[t]);
       }
 #pragma unroll
       for (int x = 0; x < EPA; ++x) {
@@ -342,8 +356,8 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int x = 0; x < EPA; x += 2) {
           const int k = i * EPA + x, tt = k >> 4, r = k & 15;
-          pb[k >> 3][k & 7] = (bf16)scur[tt][r];
-          pb[k >> 3][(k & 7) + 1] = (bf16)scur[tt][r + 1];
+          pb[k >> 3][k & 7] = (E)scur[tt][r];
+          pb[k >> 3][(k & 7) + 1] = (E)scur[tt][r + 1];
         }
       }
       __builtin_amdgcn_sched_barrier(0);  // nothing crosses: keeps the ring one MFMA ahead
@@ -364,30 +378,30 @@ void fwd_bf16_kernel(FwdParams p) {
                 (w[x] >= p.drop_threshold) ? scur[t][4 * g + x] * p.drop_scale : 0.0f;
         }
 #pragma unroll
-      for (int k = 0; k < 32; ++k) pb[k >> 3][k & 7] = (bf16)scur[k >> 4][k & 15];
+      for (int k = 0; k < 32; ++k) pb[k >> 3][k & 7] = (E)scur[k >> 4][k & 15];
     }
     // chunk cc of pb covers keys 16cc .. 16cc+15; its k-slots match V^T below.
 
     // ---- phase B
     __builtin_amdgcn_s_setprio(0);
     if constexpr (HAS_NEXT && MASK_NEXT) apply_mask(j + 1, sn);
-    const lds_bf16* vs = to_lds(vbuf(PAR));
+    const lds_bf16* vs = (const lds_bf16*)vbuf(PAR);
     auto vread = [&](int idx) {
       const int u = idx / 4, cc = idx % 4;
-      const bf16x4 lo = lds_read_tr4(vs + voff[0][u] + 16 * cc * D);
-      const bf16x4 hi4 = lds_read_tr4(vs + voff[1][u] + 16 * cc * D);
-      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      const V4 lo = __builtin_bit_cast(V4, lds_read_tr4(vs + voff[0][u] + 16 * cc * D));
+      const V4 hi4 = __builtin_bit_cast(V4, lds_read_tr4(vs + voff[1][u] + 16 * cc * D));
+      const V8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       return a;
     };
     float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    bf16x8 va[3];
+    V8 va[3];
     va[0] = vread(0);
     va[1] = vread(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int idx = 0; idx < NB; ++idx) {
       if (idx + 2 < NB) va[(idx + 2) % 3] = vread(idx + 2);
-      oacc[idx / 4] = mfma32(va[idx % 3], pb[idx % 4], oacc[idx / 4]);
+      oacc[idx / 4] = Elem<E>::mma(va[idx % 3], pb[idx % 4], oacc[idx / 4]);
       if constexpr (HAS_NEXT) {
 #pragma unroll
         for (int x = 0; x < MPB; x += 2) {
@@ -455,9 +469,9 @@ void fwd_bf16_kernel(FwdParams p) {
   } else {
     __syncthreads();
     {
-      bf16* ot = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
-      acc_rows_to_lds<D>(ot, oacc, inv, false, li, hh);
-      lds_rows_to_global<D>(ot, p.o + head_off + (size_t)qw * D, N - qw, lane);
+      E* ot = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
+      acc_rows_to_lds<D, E>(ot, oacc, inv, false, li, hh);
+      lds_rows_to_global_strided<D, E>(ot, og + (int64_t)qw * p.so.n, p.so.n, N - qw, lane);
     }
     if (qi < N && hh == 0) p.lse[(size_t)head * N + qi] = lse_out;
   }
@@ -467,29 +481,30 @@ void fwd_bf16_kernel(FwdParams p) {
 // fp32 path: one thread per query row, K/V tiles of 64 keys staged in LDS and
 // read as broadcasts; online softmax over each tile in fp32 registers.
 template <int D>
-__global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q,
-                                                     const float* __restrict__ k,
-                                                     const float* __restrict__ v,
-                                                     float* __restrict__ o, float* __restrict__ lse,
-                                                     const int32_t* key_lens, int H, int N,
-                                                     int causal, float scale_log2) {
+__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
   constexpr int BN = 64;
   __shared__ float ks[BN][D];
   __shared__ float vs[BN][D];
+  const int N = p.N;
   const int nqb = (N + 63) / 64;
   const int head = blockIdx.x / nqb;
   const int qb = blockIdx.x - head * nqb;
-  const int bi = head / H;
+  const int bi = head / p.H, hi = head - bi * p.H;
   const int qi = qb * 64 + threadIdx.x;
+  const int causal = p.causal;
   int L = N;
-  if (key_lens) L = min(max(key_lens[bi], 0), N);
+  if (p.key_lens) L = min(max(p.key_lens[bi], 0), N);
   const int kend = causal ? min(L, qb * 64 + 64) : L;
-  const size_t off = (size_t)head * N * D;
+  const float* qg = (const float*)p.q + (bi * p.sq.b + hi * p.sq.h);
+  const float* kg = (const float*)p.k + (bi * p.sk.b + hi * p.sk.h);
+  const float* vg = (const float*)p.v + (bi * p.sv.b + hi * p.sv.h);
+  float* og = (float*)p.o + (bi * p.so.b + hi * p.so.h);
+  const float scale_log2 = p.scale_log2;
 
   float qr[D], acc[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    qr[c] = qi < N ? q[off + (size_t)qi * D + c] : 0.0f;
+    qr[c] = qi < N ? qg[(int64_t)qi * p.sq.n + c] : 0.0f;
     acc[c] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
@@ -497,8 +512,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
     __syncthreads();
     for (int idx = threadIdx.x; idx < BN * D; idx += 64) {
       const int row = kb + idx / D;
-      ks[idx / D][idx % D] = row < N ? k[off + (size_t)row * D + idx % D] : 0.0f;
-      vs[idx / D][idx % D] = row < N ? v[off + (size_t)row * D + idx % D] : 0.0f;
+      ks[idx / D][idx % D] = row < N ? kg[(int64_t)row * p.sk.n + idx % D] : 0.0f;
+      vs[idx / D][idx % D] = row < N ? vg[(int64_t)row * p.sv.n + idx % D] : 0.0f;
     }
     __syncthreads();
     float s[BN];
@@ -529,8 +544,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
   if (qi < N) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-    for (int c = 0; c < D; ++c) o[off + (size_t)qi * D + c] = acc[c] * inv;
-    lse[(size_t)head * N + qi] = l > 0.0f ? (m * scale_log2 + log2f(l)) * kLn2 : -INFINITY;
+    for (int c = 0; c < D; ++c) og[(int64_t)qi * p.so.n + c] = acc[c] * inv;
+    p.lse[(size_t)head * N + qi] = l > 0.0f ? (m * scale_log2 + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -538,28 +553,26 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
 // m_i = max_s LSE_i^(s), and LSE_i = m_i + ln sum_s w_s (each split's O is
 // normalised by its own row sum l_s, and exp(LSE^(s)) = l_s e^(m_s)).  Eight
 // columns per thread; a row whose splits all saw no key gets O = 0, LSE = -inf.
-template <int D>
-__global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restrict__ opart,
-                                                          const float* __restrict__ lsepart,
-                                                          bf16* __restrict__ o,
-                                                          float* __restrict__ lse, int64_t rows,
-                                                          int splits) {
+template <typename E, int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(FwdParams p, int64_t rows) {
+  typedef E v8 __attribute__((ext_vector_type(8)));
   constexpr int LPR = D / 8;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = t / LPR;
   const int c = (int)(t % LPR);
   if (row >= rows) return;
+  const int splits = p.num_splits;
   float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, lsepart[(int64_t)s * rows + row]);
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, p.lsepart[(int64_t)s * rows + row]);
   float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   float den = 0.0f;
   if (m != -INFINITY) {
     for (int s = 0; s < splits; ++s) {
-      const float ls = lsepart[(int64_t)s * rows + row];
+      const float ls = p.lsepart[(int64_t)s * rows + row];
       if (ls == -INFINITY) continue;
       const float wgt = __expf(ls - m);
       den += wgt;
-      const float* src = opart + ((int64_t)s * rows + row) * D + 8 * c;
+      const float* src = p.opart + ((int64_t)s * rows + row) * D + 8 * c;
       const f32x4 a = *(const f32x4*)src, b = *(const f32x4*)(src + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -569,85 +582,100 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restric
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  bf16x8 ov;
+  v8 ov;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ov[e] = (bf16)(acc[e] * inv);
-  *(bf16x8*)(o + row * D + 8 * c) = ov;
-  if (c == 0) lse[row] = den > 0.0f ? m + __logf(den) : -INFINITY;
+  for (int e = 0; e < 8; ++e) ov[e] = (E)(acc[e] * inv);
+  const int head = (int)(row / p.N), n = (int)(row - (int64_t)head * p.N);
+  const int bi = head / p.H, hi = head - bi * p.H;
+  E* dst = (E*)p.o + (bi * p.so.b + hi * p.so.h + (int64_t)n * p.so.n) + 8 * c;
+  *(v8*)dst = ov;
+  if (c == 0) p.lse[row] = den > 0.0f ? m + __logf(den) : -INFINITY;
 }
 
-template <int D, bool CAUSAL, bool DROPOUT, bool SPLIT>
-hipError_t launch_bf16(const FwdParams& p, int heads, hipStream_t s) {
+template <typename E, int D, bool CAUSAL, bool DROPOUT, bool SPLIT>
+hipError_t launch(const FwdParams& p, int heads, hipStream_t s) {
   using C = FwdCfg<D>;
   const int grid = heads * (SPLIT ? p.num_qblocks * p.num_splits
                                   : CAUSAL ? (p.num_qblocks + 1) / 2 : p.num_qblocks);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROPOUT, SPLIT>), dim3(grid), dim3(C::THREADS), 0,
-                     s, p);
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, DROPOUT, SPLIT>), dim3(grid), dim3(C::THREADS), 0, s,
+                     p);
   hipError_t e = hipGetLastError();
   if (!SPLIT || e != hipSuccess) return e;
   const int64_t rows = (int64_t)heads * p.N;
   const int64_t threads = rows * (D / 8);
-  hipLaunchKernelGGL(fwd_combine_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     (const float*)p.opart, (const float*)p.lsepart, p.o, p.lse, rows, p.num_splits);
+  hipLaunchKernelGGL((fwd_combine_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                     0, s, p, rows);
   return hipGetLastError();
 }
 
-template <int D, bool SPLIT>
-hipError_t dispatch_bf16(const FwdParams& p, int heads, bool causal, bool dropout, hipStream_t s) {
+template <typename E, int D, bool SPLIT>
+hipError_t dispatch(const FwdParams& p, int heads, bool causal, bool dropout, hipStream_t s) {
   if (causal) {
-    return dropout ? launch_bf16<D, true, true, SPLIT>(p, heads, s)
-                   : launch_bf16<D, true, false, SPLIT>(p, heads, s);
+    return dropout ? launch<E, D, true, true, SPLIT>(p, heads, s)
+                   : launch<E, D, true, false, SPLIT>(p, heads, s);
   }
-  return dropout ? launch_bf16<D, false, true, SPLIT>(p, heads, s)
-                 : launch_bf16<D, false, false, SPLIT>(p, heads, s);
+  return dropout ? launch<E, D, false, true, SPLIT>(p, heads, s)
+                 : launch<E, D, false, false, SPLIT>(p, heads, s);
 }
 
-}  // namespace
+template <typename E>
+hipError_t dispatch_d(FwdParams& p, const FwdArgs& a, hipStream_t s) {
+  const bool dropout = a.dropout_p > 0.0f;
+  const int heads = a.B * a.H;
+  const bool split = a.num_splits > 0;
+  const bool causal = a.causal != 0;
+  if (a.d == 64) {
+    p.num_qblocks = (a.N + FwdCfg<64>::BM - 1) / FwdCfg<64>::BM;
+    return split ? dispatch<E, 64, true>(p, heads, causal, dropout, s)
+                 : dispatch<E, 64, false>(p, heads, causal, dropout, s);
+  }
+  p.num_qblocks = (a.N + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
+  return split ? dispatch<E, 128, true>(p, heads, causal, dropout, s)
+               : dispatch<E, 128, false>(p, heads, causal, dropout, s);
+}
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+FwdParams make_params(const FwdArgs& a) {
   FwdParams p;
-  p.q = (const bf16*)a.q;
-  p.k = (const bf16*)a.k;
-  p.v = (const bf16*)a.v;
-  p.o = (bf16*)a.o;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
   p.lse = a.lse;
   p.key_lens = a.key_lens;
+  p.sq = a.sq;
+  p.sk = a.sk;
+  p.sv = a.sv;
+  p.so = a.so;
   p.H = a.H;
   p.N = a.N;
+  p.num_qblocks = 0;
+  p.causal = a.causal != 0;
   p.scale_log2 = a.scale * kLog2e;
   p.drop_threshold = a.drop_threshold;
   p.drop_scale = a.drop_scale;
   p.seed_lo = (uint32_t)(a.seed & 0xffffffffu);
   p.seed_hi = (uint32_t)(a.seed >> 32);
-  const bool dropout = a.dropout_p > 0.0f;
-  const int heads = a.B * a.H;
   p.opart = a.opart;
   p.lsepart = a.lsepart;
   p.num_splits = a.num_splits;
-  p.heads = heads;
-  const bool split = a.num_splits > 0;
-  if (a.d == 64) {
-    p.num_qblocks = (a.N + FwdCfg<64>::BM - 1) / FwdCfg<64>::BM;
-    return split ? dispatch_bf16<64, true>(p, heads, a.causal != 0, dropout, s)
-                 : dispatch_bf16<64, false>(p, heads, a.causal != 0, dropout, s);
-  }
-  p.num_qblocks = (a.N + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
-  return split ? dispatch_bf16<128, true>(p, heads, a.causal != 0, dropout, s)
-               : dispatch_bf16<128, false>(p, heads, a.causal != 0, dropout, s);
+  p.heads = a.B * a.H;
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_16(const FwdArgs& a, hipStream_t s) {
+  FwdParams p = make_params(a);
+  return a.fp16 ? dispatch_d<f16>(p, a, s) : dispatch_d<bf16>(p, a, s);
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
+  FwdParams p = make_params(a);
   const int grid = a.B * a.H * ((a.N + 63) / 64);
-  const float sl = a.scale * kLog2e;
-  if (a.d == 64) {
-    hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3(grid), dim3(64), 0, s, (const float*)a.q,
-                       (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.key_lens, a.H,
-                       a.N, a.causal, sl);
-  } else {
-    hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3(grid), dim3(64), 0, s, (const float*)a.q,
-                       (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.key_lens, a.H,
-                       a.N, a.causal, sl);
-  }
+  if (a.d == 64)
+    hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3(grid), dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3(grid), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -7,12 +7,23 @@
 
 namespace fa {
 
+// Element strides (batch, head, row) of a [B, H, N, d]-indexed tensor whose
+// head dimension is contiguous.
+struct Strides {
+  int64_t b, h, n;
+};
+inline Strides contiguous_bhnd(int H, int N, int d) {
+  return Strides{(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
+}
+
 struct FwdArgs {
+  bool fp16 = false;  // 16-bit element type: fp16 instead of bf16
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;
+  Strides sq, sk, sv, so;
   int B, H, N, d;
   float scale;
   int causal;
@@ -30,6 +41,7 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
+  bool fp16 = false;  // 16-bit element type: fp16 instead of bf16
   const void* q;
   const void* k;
   const void* v;
@@ -39,6 +51,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, N, d;
   float scale;
   int causal;
@@ -52,7 +65,7 @@ struct BwdArgs {
 };
 
 // Each returns hipSuccess or the launch error.
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_16(const FwdArgs& a, hipStream_t s);  // bf16 or fp16
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 // Backward stages, selected by a bit mask and launched in this order: the
 // per-row preprocessing alone (D and LSE*log2e into the workspace), the dQ
@@ -60,6 +73,6 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 // workspace), the dK/dV kernel (which reads them).  The full backward is
 // kBwdQ | kBwdKV.
 enum : int { kBwdPre = 1, kBwdKV = 2, kBwdQ = 4, kBwdAll = kBwdQ | kBwdKV };
-hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
+hipError_t launch_bwd_16(const BwdArgs& a, int stages, hipStream_t s);  // bf16 or fp16
 
 }  // namespace fa
