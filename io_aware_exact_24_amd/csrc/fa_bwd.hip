@@ -308,13 +308,14 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int c = 0; c < KC; ++c)
       kdst[c] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(krs, krow + 32 * c, 0, 0));
     const int r = wrow + lane / C::CHUNKS, pc = lane % C::CHUNKS;
-    const uint32_t ldl_v = (uint32_t)((lane / C::CHUNKS) * svn + (pc ^ swz<D>(r)) * 8) * ES;
+    const uint32_t vrb = (uint32_t)svn * ES;
+    const uint32_t vbase =
+        tile_offset((uint32_t)((lane / C::CHUNKS) * svn + (pc ^ swz<D>(r)) * 8) * ES, kb_ + wrow, vrb);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i)
-        lds_dma16_row(vrs, skv + h * TILE + (i * NW + wave) * 512, ldl_v, kb_ + h * BQ + i * COPY_ROWS + wrow,
-                      (uint32_t)svn * ES);
+        lds_dma16(vrs, skv + h * TILE + (i * NW + wave) * 512, vbase + (h * BQ + i * COPY_ROWS) * vrb);
   };
 
   // Copy piece x of tile `it` into stage s: pieces 0 .. 2*LOADS-1 are this
@@ -322,23 +323,33 @@ void bwd_dkdv_kernel(BwdParams p) {
   // LSE*log2e, waves 2-3 copy D: duplicates of the same values, no branch).
   // Tiles past the end read as zero.
   constexpr int NPIECE = 2 * C::LOADS + 1;
-  auto issue_piece = [&](int it, auto s, auto x_t) __attribute__((always_inline)) {
+  // Per-lane offsets of tile it's first Q and dO copies (formed once per tile).
+  const uint32_t qrb = (uint32_t)sqn * ES, orb = (uint32_t)son_ * ES;
+  const uint32_t qstep = COPY_ROWS * qrb, ostep = COPY_ROWS * orb;
+  struct TileAt {
+    int it;
+    uint32_t q, o;
+  };
+  auto tile_at = [&](int it) __attribute__((always_inline)) {
+    return TileAt{it, tile_offset(ldl_q, it * BQ + wrow, qrb), tile_offset(ldl_o, it * BQ + wrow, orb)};
+  };
+  auto issue_piece = [&](const TileAt& tl, auto s, auto x_t) __attribute__((always_inline)) {
     constexpr int x = decltype(x_t)::value;
     if constexpr (x < 2 * C::LOADS) {
       constexpr int i = x / 2;
-      const int row0 = it * BQ + i * COPY_ROWS + wrow;  // wave-uniform
       if constexpr (x % 2 == 0)
-        lds_dma16_row(qrs, qst(s) + (i * NW + wave) * 512, ldl_q, row0, (uint32_t)sqn * ES);
+        lds_dma16(qrs, qst(s) + (i * NW + wave) * 512, tl.q + i * qstep);
       else
-        lds_dma16_row(ors, ost(s) + (i * NW + wave) * 512, ldl_o, row0, (uint32_t)son_ * ES);
+        lds_dma16(ors, ost(s) + (i * NW + wave) * 512, tl.o + i * ostep);
     } else {
       const bool dv = wave >= 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(dv ? drs : lrs, (lds_void_t*)(dv ? dst(s) : lst(s)), 4,
-                                               (uint32_t)(it * BQ + lane) * 4, 0, 0, 0);
+                                               (uint32_t)(tl.it * BQ + lane) * 4, 0, 0, 0);
     }
   };
   auto issue_tile = [&](int it, auto s) __attribute__((always_inline)) {
-    static_for<NPIECE>([&](auto x_t) __attribute__((always_inline)) { issue_piece(it, s, x_t); });
+    const TileAt tl = tile_at(it);
+    static_for<NPIECE>([&](auto x_t) __attribute__((always_inline)) { issue_piece(tl, s, x_t); });
   };
 
   // LDS element offsets of the operand reads.  Row reads (A operand of S and
@@ -529,6 +540,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
       });
     };
+    const TileAt tn = tile_at(t + 2);  // this body's copies
     __builtin_amdgcn_sched_barrier(0);
     static_for<NOPS>([&](auto i_t) __attribute__((always_inline)) {
       constexpr int i = decltype(i_t)::value;
@@ -537,7 +549,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       // copies of tile t+2, one piece every other MFMA (a burst of them
       // stalls the wave on the full memory queue)
       if constexpr (i % 2 == 0 && i / 2 < NPIECE)
-        issue_piece(t + 2, S2{}, std::integral_constant<int, i / 2>{});
+        issue_piece(tn, S2{}, std::integral_constant<int, i / 2>{});
       constexpr int ph = i / NP, j = i % NP;
       const V8& a = ring[i % RG];
       if constexpr (ph == 0) {
@@ -618,8 +630,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     acc_rows_to_lds<D, E>(kt, dkacc, p.scale, zero, li, hh);
     acc_rows_to_lds<D, E>(vt, dvacc, 1.0f, zero, li, hh);
     const int row0 = kb + 32 * wave;
-    lds_rows_to_global_strided<D, E>(kt, dkg + (int64_t)row0 * p.sdk.n, p.sdk.n, N - row0, lane);
-    lds_rows_to_global_strided<D, E>(vt, dvg + (int64_t)row0 * p.sdv.n, p.sdv.n, N - row0, lane);
+    lds_rows_to_buffer<D, E>(kt, dkg + (int64_t)row0 * p.sdk.n, p.sdk.n, N - row0, lane);
+    lds_rows_to_buffer<D, E>(vt, dvg + (int64_t)row0 * p.sdv.n, p.sdv.n, N - row0, lane);
   }
   prefetched = !DROPOUT && has_next;
   }  // block
@@ -667,6 +679,15 @@ void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
+  // (b, h) slices through per-tensor strides (both items of a workgroup are
+  // in the same head)
+  const E* qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h);
+  const E* kg = (const E*)p.k + (bi * p.sk.b + hi * p.sk.h);
+  const E* vg = (const E*)p.v + (bi * p.sv.b + hi * p.sv.h);
+  const E* dog = (const E*)p.dout + (bi * p.sdo.b + hi * p.sdo.h);
+  const E* og = (const E*)p.o + (bi * p.so.b + hi * p.so.h);
+  E* dqg = (E*)p.dq + (bi * p.sdq.b + hi * p.sdq.h);
+  const int sqn = (int)p.sq.n, skn = (int)p.sk.n, svn = (int)p.sv.n, son_ = (int)p.sdo.n;
   for (int item = 0; item < nitems; ++item) {
   if (item) __syncthreads();  // every wave is done with the first block's tiles
   const int qb = CAUSAL ? (item == 0 ? nqb - 1 - w : w) : w;
@@ -682,14 +703,6 @@ void bwd_dq_kernel(BwdParams p) {
   if (CAUSAL) nfree = min(nfree, q0 / BN);
   nfree = min(nfree, nkb);
 
-  // (b, h) slices through per-tensor strides
-  const E* qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h);
-  const E* kg = (const E*)p.k + (bi * p.sk.b + hi * p.sk.h);
-  const E* vg = (const E*)p.v + (bi * p.sv.b + hi * p.sv.h);
-  const E* dog = (const E*)p.dout + (bi * p.sdo.b + hi * p.sdo.h);
-  const E* og = (const E*)p.o + (bi * p.so.b + hi * p.so.h);
-  E* dqg = (E*)p.dq + (bi * p.sdq.b + hi * p.sdq.h);
-  const int sqn = (int)p.sq.n, skn = (int)p.sk.n, svn = (int)p.sv.n, son_ = (int)p.sdo.n;
   // Q^T and dO^T as B operands (k = head dimension): lane holds row qi,
   // elements 16c + 8hh .. +7, read from LDS after the block's rows have been
   // copied in (below).
@@ -718,19 +731,28 @@ void bwd_dq_kernel(BwdParams p) {
     ldl_k = (uint32_t)(crow * skn + lch) * ES;
     ldl_v = (uint32_t)(crow * svn + lch) * ES;
   }
-  // Copy piece x of tile jt (x < LOADS: K, else V) into stage S.
-  auto issue_piece = [&](int jt, auto par_t, int x) {
+  // Per-lane offsets of tile jt's first K and V copies (formed once per tile).
+  const uint32_t krb = (uint32_t)skn * ES, vrb = (uint32_t)svn * ES;
+  const uint32_t kstep = COPY_ROWS * krb, vstep = COPY_ROWS * vrb;
+  struct TileAt {
+    uint32_t k, v;
+  };
+  auto tile_at = [&](int jt) {
+    return TileAt{tile_offset(ldl_k, jt * BN + wrow, krb), tile_offset(ldl_v, jt * BN + wrow, vrb)};
+  };
+  // Copy piece x of a tile (x < LOADS: K, else V) into stage S.
+  auto issue_piece = [&](const TileAt& tl, auto par_t, int x) {
     constexpr int S = decltype(par_t)::value;
     const int i = x % C::LOADS;
-    const int row0 = jt * BN + i * COPY_ROWS + wrow;  // wave-uniform
     if (x < C::LOADS)
-      lds_dma16_row(krs, (S ? sk1 : sk0) + (i * NW + wave) * 512, ldl_k, row0, (uint32_t)skn * ES);
+      lds_dma16(krs, (S ? sk1 : sk0) + (i * NW + wave) * 512, tl.k + i * kstep);
     else
-      lds_dma16_row(vrs, (S ? sv1 : sv0) + (i * NW + wave) * 512, ldl_v, row0, (uint32_t)svn * ES);
+      lds_dma16(vrs, (S ? sv1 : sv0) + (i * NW + wave) * 512, tl.v + i * vstep);
   };
   auto issue = [&](int jt, auto par_t) {
+    const TileAt tl = tile_at(jt);
 #pragma unroll
-    for (int x = 0; x < 2 * C::LOADS; ++x) issue_piece(jt, par_t, x);
+    for (int x = 0; x < 2 * C::LOADS; ++x) issue_piece(tl, par_t, x);
   };
   // Row reads of K and V tiles (A operands of S^T and dP^T): row 32t + li,
   // logical chunk 2c + hh.  Transposing reads of the K tile (A operand of
@@ -749,13 +771,14 @@ void bwd_dq_kernel(BwdParams p) {
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(dog, rows_bytes(N, son_, D, ES));
     const uint32_t ldl_q = (uint32_t)(crow * sqn + lch) * ES;
     const uint32_t ldl_o = (uint32_t)(crow * son_ + lch) * ES;
+    const uint32_t qrb = (uint32_t)sqn * ES, orb = (uint32_t)son_ * ES;
+    const uint32_t qb = tile_offset(ldl_q, q0 + wrow, qrb), ob = tile_offset(ldl_o, q0 + wrow, orb);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int row0 = q0 + i * COPY_ROWS + wrow;  // wave-uniform
-      lds_dma16_row(qrs, sk0 + (i * NW + wave) * 512, ldl_q, row0, (uint32_t)sqn * ES);
-      lds_dma16_row(qrs, sk1 + (i * NW + wave) * 512, ldl_q, row0 + BN, (uint32_t)sqn * ES);
-      lds_dma16_row(ors, sv0 + (i * NW + wave) * 512, ldl_o, row0, (uint32_t)son_ * ES);
-      lds_dma16_row(ors, sv1 + (i * NW + wave) * 512, ldl_o, row0 + BN, (uint32_t)son_ * ES);
+      lds_dma16(qrs, sk0 + (i * NW + wave) * 512, qb + (i * COPY_ROWS) * qrb);
+      lds_dma16(qrs, sk1 + (i * NW + wave) * 512, qb + (i * COPY_ROWS + BN) * qrb);
+      lds_dma16(ors, sv0 + (i * NW + wave) * 512, ob + (i * COPY_ROWS) * orb);
+      lds_dma16(ors, sv1 + (i * NW + wave) * 512, ob + (i * COPY_ROWS + BN) * orb);
     }
     wait_vmem();
     __syncthreads();
@@ -816,6 +839,7 @@ void bwd_dq_kernel(BwdParams p) {
     const f32x16 zero = {};
     constexpr int NS = 4 * KC;
     V8 ring[3];
+    const TileAt tn = tile_at(j + 1);  // this tile's copies of the next one
     auto sread = [&](int i) {
       const int m = i / KC, c = i % KC;
       return *(const V8*)((m < 2 ? ks : vs) + roff[c] + (m & 1) * 32 * D);
@@ -856,7 +880,7 @@ void bwd_dq_kernel(BwdParams p) {
       // wave on the full memory queue); a tile past the end reads as zero
       // into a stage nothing reads again
       if (i % 2 == 0 && i / 2 < 2 * C::LOADS)
-        issue_piece(j + 1, std::integral_constant<int, S ^ 1>{}, i / 2);
+        issue_piece(tn, std::integral_constant<int, S ^ 1>{}, i / 2);
       if (i + 2 < NS) ring[(i + 2) % 3] = sread(i + 2);
       const int m = i / KC, c = i % KC;
       f32x16& acc = m < 2 ? sacc[m & 1] : pacc[m & 1];
@@ -922,7 +946,7 @@ void bwd_dq_kernel(BwdParams p) {
     const int qw = q0 + wave * 32;
     E* qt = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
     acc_rows_to_lds<D, E>(qt, qacc, p.scale, false, li, hh);
-    lds_rows_to_global_strided<D, E>(qt, dqg + (int64_t)qw * p.sdq.n, p.sdq.n, N - qw, lane);
+    lds_rows_to_buffer<D, E>(qt, dqg + (int64_t)qw * p.sdq.n, p.sdq.n, N - qw, lane);
   }
   }  // item
 }

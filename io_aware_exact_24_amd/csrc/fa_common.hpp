@@ -245,6 +245,14 @@ struct Elem<f16> {
   }
 };
 
+// Buffer resource for raw byte-addressed loads from [base, base + bytes).  A
+// load whose 16-byte range lies past `bytes` returns zeros, which gives the
+// ragged tail of a sequence for free.  The last word selects 32-bit raw
+// buffer access on gfx9-family parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Bytes a buffer resource must span to cover rows [0, rows) of D elements
 // each, `sn` elements apart (sn >= D): reads of any row >= rows then fall
 // outside it and return zeros.
@@ -274,35 +282,29 @@ __device__ __forceinline__ void acc_rows_to_lds(E* tile, const f32x16 (&acc)[D /
     }
 }
 
-// Copy rows [0, min(nrows, 32)) of such an LDS tile to global memory at dst
-// (row stride D elements), 16 bytes per lane: every store instruction writes
-// 64 / (D/8) whole rows, contiguous in memory.
-template <int D>
-__device__ __forceinline__ void lds_rows_to_global(const bf16* tile, bf16* dst, int nrows, int lane) {
-  constexpr int CH = D / 8, RPI = 64 / CH;
-  asm volatile("" : "+v"(lane));  // see acc_rows_to_lds
-  const int c = lane % CH;
-#pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int r = i * RPI + lane / CH;
-    const bf16x8 v = *(const bf16x8*)(tile + r * D + ((c ^ swz<D>(r)) * 8));
-    if (r < nrows) *(bf16x8*)(dst + (size_t)r * D + c * 8) = v;
-  }
-}
-
-// The same copy to rows `sn` elements apart (rows [0, min(nrows, 32))).
+// Copy rows [0, min(nrows, 32)) of such an LDS tile to the rows of a tensor
+// slice starting at dst, rows `sn` elements apart, 16 bytes per lane: every
+// store instruction writes 64 / (D/8) whole rows.  The stores go through a
+// buffer resource whose byte range ends with row min(nrows, 32) - 1, so the
+// range check drops the rows past it (no branch; one 32-bit per-lane offset
+// plus a uniform step per row: callers keep each slice's byte span within
+// 32 bits).
 template <int D, typename E>
-__device__ __forceinline__ void lds_rows_to_global_strided(const E* tile, E* dst, int64_t sn,
-                                                           int nrows, int lane) {
-  constexpr int CH = D / 8, RPI = 64 / CH;
+__device__ __forceinline__ void lds_rows_to_buffer(const E* tile, E* dst, int64_t sn, int nrows,
+                                                   int lane) {
+  constexpr int CH = D / 8, RPI = 64 / CH, ES = (int)sizeof(E);
   typedef E v8 __attribute__((ext_vector_type(8)));
   asm volatile("" : "+v"(lane));  // see acc_rows_to_lds
   const int c = lane % CH;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, rows_bytes(min(nrows, 32), sn, D, ES));
+  const uint32_t rb = (uint32_t)sn * ES;
+  const uint32_t off0 = (uint32_t)(lane / CH) * rb + (uint32_t)(c * 8 * ES);
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CH;
     const v8 v = *(const v8*)(tile + r * D + ((c ^ swz<D>(r)) * 8));
-    if (r < nrows) *(v8*)(dst + (int64_t)r * sn + c * 8) = v;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off0 + (uint32_t)(i * RPI) * rb,
+                                           0, 0);
   }
 }
 
@@ -316,13 +318,6 @@ __device__ __forceinline__ int xcd_remap(int p, int G) {
 }
 
 
-// Buffer resource for raw byte-addressed loads from [base, base + bytes).  A
-// load whose 16-byte range lies past `bytes` returns zeros, which gives the
-// ragged tail of a sequence for free.  The last word selects 32-bit raw
-// buffer access on gfx9-family parts.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -334,20 +329,20 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, const void* 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, voff, 0, 0, 0);
 }
 
-// The same for the wave-uniform tile row `row0` of a tensor whose rows are
-// `row_bytes` apart: lane data from byte row0 * row_bytes + voff.  The row
-// offset goes into the per-lane offset, not the instruction's scalar-offset
-// field: the buffer range check that turns reads past the last row into
-// zeros looks at the per-lane offset (plus the immediate) only, so a row
-// offset in the scalar field would let tiles past the end read whatever
-// memory follows the slice.  row0 is made opaque (kept in a scalar register)
-// so that the product is formed at the copy, not hoisted out of the loop as
-// one register per copy.
-__device__ __forceinline__ void lds_dma16_row(__amdgpu_buffer_rsrc_t r, const void* lds_wave_base,
-                                              uint32_t voff, int row0, uint32_t row_bytes) {
+// Per-lane byte offset of a tile's first copy: voff + row0 * row_bytes for
+// the wave-uniform first row row0.  Copy i of the tile then adds the
+// wave-uniform i * (rows per copy round) * row_bytes.  Row offsets belong in
+// the per-lane offset, never the instruction's scalar-offset field: the
+// buffer range check that turns reads past the last row into zeros looks at
+// the per-lane offset (plus the immediate) only, so a row offset in the
+// scalar field would let tiles past the end read whatever memory follows
+// the slice.  row0 is made opaque (kept in a scalar register) so that the
+// base is formed once per tile where it is needed, instead of the whole sum
+// being hoisted out of the loop as one register per copy.
+__device__ __forceinline__ uint32_t tile_offset(uint32_t voff, int row0, uint32_t row_bytes) {
+  row0 = __builtin_amdgcn_readfirstlane(row0);  // uniform by construction
   asm volatile("" : "+s"(row0));
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16,
-                                           voff + (uint32_t)row0 * row_bytes, 0, 0, 0);
+  return voff + (uint32_t)row0 * row_bytes;
 }
 
 // Marks x as still in use at this point (see keep).

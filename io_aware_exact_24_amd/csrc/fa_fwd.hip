@@ -72,7 +72,7 @@ struct FwdCfg {
   static_assert(LOADS * THREADS == BN * CHUNKS, "tile/thread mismatch");
 };
 
-template <typename E, int D, bool CAUSAL, bool DROPOUT, bool SPLIT>
+template <typename E, int D, bool CAUSAL, bool DROPOUT, bool SPLIT, bool CONTIG>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
@@ -108,6 +108,16 @@ void fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
+  // (b, h) slices through per-tensor strides; rows are p.s?.n elements apart
+  // (both items of a workgroup are in the same head).
+  const E* __restrict__ qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h);
+  const E* kg = (const E*)p.k + (bi * p.sk.b + hi * p.sk.h);
+  const E* vg = (const E*)p.v + (bi * p.sv.b + hi * p.sv.h);
+  E* og = (E*)p.o + (bi * p.so.b + hi * p.so.h);
+  // Row strides; CONTIG: every row is d elements after the previous one, known
+  // at compile time, so tile offsets fold into constants.
+  const int sqn = CONTIG ? D : (int)p.sq.n, skn = CONTIG ? D : (int)p.sk.n;
+  const int svn = CONTIG ? D : (int)p.sv.n, son = CONTIG ? D : (int)p.so.n;
   for (int item = 0; item < nitems; ++item) {
   if (item) __syncthreads();  // every wave is done with the first block's tiles
   int qb = CAUSAL ? (item == 0 ? nqb - 1 - w : w) : w;
@@ -135,12 +145,6 @@ void fwd_kernel(FwdParams p) {
     nfree = min(max(nfree - jt0, 0), nkb);
   }
 
-  // (b, h) slices through per-tensor strides; rows are p.s?.n elements apart.
-  const E* __restrict__ qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h);
-  const E* kg = (const E*)p.k + (bi * p.sk.b + hi * p.sk.h);
-  const E* vg = (const E*)p.v + (bi * p.sv.b + hi * p.sv.h);
-  E* og = (E*)p.o + (bi * p.so.b + hi * p.so.h);
-  const int skn = (int)p.sk.n, svn = (int)p.sv.n;
   // The copies cover the tiles [0, nkb) only: copies past them (issued without
   // a branch) read zeros without touching memory.
   const int krows = min((jt0 + nkb) * BN, N);
@@ -152,7 +156,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     if (qi < N) {
-      qreg[c] = *(const V8*)(qg + (int64_t)qi * p.sq.n + 16 * c + 8 * hh);
+      qreg[c] = *(const V8*)(qg + (int64_t)qi * sqn + 16 * c + 8 * hh);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qreg[c][e] = (E)0.0f;
@@ -173,21 +177,33 @@ void fwd_kernel(FwdParams p) {
     kld0 = (uint32_t)(r * skn + lch) * ES;
     vld0 = (uint32_t)(r * svn + lch) * ES;
   }
-  auto issue_k_piece = [&](int jt, int stage, int i) {
-    lds_dma16_row(krs, kbuf(stage) + (i * NW + wave) * 512, kld0, (jt0 + jt) * BN + i * C::COPY_ROWS,
-                  (uint32_t)skn * ES);
+  // Row strides in bytes, and the byte step between copy rounds.
+  const uint32_t krb = (uint32_t)skn * ES, vrb = (uint32_t)svn * ES;
+  const uint32_t kstep = C::COPY_ROWS * krb, vstep = C::COPY_ROWS * vrb;
+  // Per-lane offsets of the first copy of K and V tile jt.
+  auto k_base = [&](int jt) {
+    if constexpr (CONTIG) return kld0 + (uint32_t)((jt0 + jt) * BN * D * ES);
+    else return tile_offset(kld0, (jt0 + jt) * BN, krb);
   };
-  auto issue_v_piece = [&](int jt, int stage, int i) {
-    lds_dma16_row(vrs, vbuf(stage) + (i * NW + wave) * 512, vld0, (jt0 + jt) * BN + i * C::COPY_ROWS,
-                  (uint32_t)svn * ES);
+  auto v_base = [&](int jt) {
+    if constexpr (CONTIG) return vld0 + (uint32_t)((jt0 + jt) * BN * D * ES);
+    else return tile_offset(vld0, (jt0 + jt) * BN, vrb);
+  };
+  auto issue_k_piece = [&](uint32_t base, int stage, int i) {
+    lds_dma16(krs, kbuf(stage) + (i * NW + wave) * 512, base + i * kstep);
+  };
+  auto issue_v_piece = [&](uint32_t base, int stage, int i) {
+    lds_dma16(vrs, vbuf(stage) + (i * NW + wave) * 512, base + i * vstep);
   };
   auto issue_k = [&](int jt, int stage) {
+    const uint32_t base = k_base(jt);
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) issue_k_piece(jt, stage, i);
+    for (int i = 0; i < C::LOADS; ++i) issue_k_piece(base, stage, i);
   };
   auto issue_v = [&](int jt, int stage) {
+    const uint32_t base = v_base(jt);
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) issue_v_piece(jt, stage, i);
+    for (int i = 0; i < C::LOADS; ++i) issue_v_piece(base, stage, i);
   };
 
   // LDS element offsets of the MFMA operand reads (stage 0; stage 1 adds TILE).
@@ -324,6 +340,7 @@ void fwd_kernel(FwdParams p) {
       ka[0] = kread(0);
       ka[1] = kread(1);
     }
+    const uint32_t kb2 = k_base(j + 2), vb1 = v_base(j + 1);  // this step's copies
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
@@ -334,9 +351,9 @@ void fwd_kernel(FwdParams p) {
       if (i % 2 == 0 && i / 2 < 2 * C::LOADS) {
         const int x = i / 2;
         if (x < C::LOADS)
-          issue_k_piece(j + 2, PAR, x);
+          issue_k_piece(kb2, PAR, x);
         else
-          issue_v_piece(j + 1, PAR ^ 1, x - C::LOADS);
+          issue_v_piece(vb1, PAR ^ 1, x - C::LOADS);
       }
       if constexpr (HAS_NEXT) {
         if (i + 2 < NA) ka[(i + 2) % 3] = kread(i + 2);
@@ -471,7 +488,7 @@ void fwd_kernel(FwdParams p) {
     {
       E* ot = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
       acc_rows_to_lds<D, E>(ot, oacc, inv, false, li, hh);
-      lds_rows_to_global_strided<D, E>(ot, og + (int64_t)qw * p.so.n, p.so.n, N - qw, lane);
+      lds_rows_to_buffer<D, E>(ot, og + (int64_t)qw * son, son, N - qw, lane);
     }
     if (qi < N && hh == 0) p.lse[(size_t)head * N + qi] = lse_out;
   }
@@ -592,13 +609,13 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdParams p, int64_t r
   if (c == 0) p.lse[row] = den > 0.0f ? m + __logf(den) : -INFINITY;
 }
 
-template <typename E, int D, bool CAUSAL, bool DROPOUT, bool SPLIT>
+template <typename E, int D, bool CAUSAL, bool DROPOUT, bool SPLIT, bool CONTIG>
 hipError_t launch(const FwdParams& p, int heads, hipStream_t s) {
   using C = FwdCfg<D>;
   const int grid = heads * (SPLIT ? p.num_qblocks * p.num_splits
                                   : CAUSAL ? (p.num_qblocks + 1) / 2 : p.num_qblocks);
-  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, DROPOUT, SPLIT>), dim3(grid), dim3(C::THREADS), 0, s,
-                     p);
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, DROPOUT, SPLIT, CONTIG>), dim3(grid), dim3(C::THREADS),
+                     0, s, p);
   hipError_t e = hipGetLastError();
   if (!SPLIT || e != hipSuccess) return e;
   const int64_t rows = (int64_t)heads * p.N;
@@ -608,14 +625,28 @@ hipError_t launch(const FwdParams& p, int heads, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename E, int D, bool SPLIT>
+template <typename E, int D, bool SPLIT, bool CONTIG>
 hipError_t dispatch(const FwdParams& p, int heads, bool causal, bool dropout, hipStream_t s) {
   if (causal) {
-    return dropout ? launch<E, D, true, true, SPLIT>(p, heads, s)
-                   : launch<E, D, true, false, SPLIT>(p, heads, s);
+    return dropout ? launch<E, D, true, true, SPLIT, CONTIG>(p, heads, s)
+                   : launch<E, D, true, false, SPLIT, CONTIG>(p, heads, s);
   }
-  return dropout ? launch<E, D, false, true, SPLIT>(p, heads, s)
-                 : launch<E, D, false, false, SPLIT>(p, heads, s);
+  return dropout ? launch<E, D, false, true, SPLIT, CONTIG>(p, heads, s)
+                 : launch<E, D, false, false, SPLIT, CONTIG>(p, heads, s);
+}
+
+// Rows d elements apart in every tensor (the batch and head strides are free).
+bool rows_contiguous(const FwdParams& p, int d) {
+  return p.sq.n == d && p.sk.n == d && p.sv.n == d && p.so.n == d;
+}
+
+// The split path (small batch x heads) keeps run-time strides only.
+template <typename E, int D>
+hipError_t dispatch_s(const FwdParams& p, int heads, bool split, bool causal, bool dropout,
+                      hipStream_t s) {
+  if (split) return dispatch<E, D, true, false>(p, heads, causal, dropout, s);
+  return rows_contiguous(p, D) ? dispatch<E, D, false, true>(p, heads, causal, dropout, s)
+                               : dispatch<E, D, false, false>(p, heads, causal, dropout, s);
 }
 
 template <typename E>
@@ -626,12 +657,10 @@ hipError_t dispatch_d(FwdParams& p, const FwdArgs& a, hipStream_t s) {
   const bool causal = a.causal != 0;
   if (a.d == 64) {
     p.num_qblocks = (a.N + FwdCfg<64>::BM - 1) / FwdCfg<64>::BM;
-    return split ? dispatch<E, 64, true>(p, heads, causal, dropout, s)
-                 : dispatch<E, 64, false>(p, heads, causal, dropout, s);
+    return dispatch_s<E, 64>(p, heads, split, causal, dropout, s);
   }
   p.num_qblocks = (a.N + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
-  return split ? dispatch<E, 128, true>(p, heads, causal, dropout, s)
-               : dispatch<E, 128, false>(p, heads, causal, dropout, s);
+  return dispatch_s<E, 128>(p, heads, split, causal, dropout, s);
 }
 
 FwdParams make_params(const FwdArgs& a) {
