@@ -339,9 +339,14 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, const void* 
 // the slice.  row0 is made opaque (kept in a scalar register) so that the
 // base is formed once per tile where it is needed, instead of the whole sum
 // being hoisted out of the loop as one register per copy.
+// CONST_STRIDE: row_bytes is a compile-time constant, and the plain sum folds
+// into immediates.
+template <bool CONST_STRIDE = false>
 __device__ __forceinline__ uint32_t tile_offset(uint32_t voff, int row0, uint32_t row_bytes) {
-  row0 = __builtin_amdgcn_readfirstlane(row0);  // uniform by construction
-  asm volatile("" : "+s"(row0));
+  if constexpr (!CONST_STRIDE) {
+    row0 = __builtin_amdgcn_readfirstlane(row0);  // uniform by construction
+    asm volatile("" : "+s"(row0));
+  }
   return voff + (uint32_t)row0 * row_bytes;
 }
 

@@ -181,14 +181,8 @@ void fwd_kernel(FwdParams p) {
   const uint32_t krb = (uint32_t)skn * ES, vrb = (uint32_t)svn * ES;
   const uint32_t kstep = C::COPY_ROWS * krb, vstep = C::COPY_ROWS * vrb;
   // Per-lane offsets of the first copy of K and V tile jt.
-  auto k_base = [&](int jt) {
-    if constexpr (CONTIG) return kld0 + (uint32_t)((jt0 + jt) * BN * D * ES);
-    else return tile_offset(kld0, (jt0 + jt) * BN, krb);
-  };
-  auto v_base = [&](int jt) {
-    if constexpr (CONTIG) return vld0 + (uint32_t)((jt0 + jt) * BN * D * ES);
-    else return tile_offset(vld0, (jt0 + jt) * BN, vrb);
-  };
+  auto k_base = [&](int jt) { return tile_offset<CONTIG>(kld0, (jt0 + jt) * BN, krb); };
+  auto v_base = [&](int jt) { return tile_offset<CONTIG>(vld0, (jt0 + jt) * BN, vrb); };
   auto issue_k_piece = [&](uint32_t base, int stage, int i) {
     lds_dma16(krs, kbuf(stage) + (i * NW + wave) * 512, base + i * kstep);
   };
