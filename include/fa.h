@@ -30,9 +30,13 @@
  * values are scaled by (float)(1 / (1 - p)) computed in double.  LSE is the
  * normaliser before dropout.  The backward must receive the forward's seed and p.
  *
- * Layouts.  Q, K, V, O, dO, dQ, dK, dV: contiguous [B, H, N, d], d innermost,
- * element type `dtype`.  LSE: contiguous fp32 [B, H, N].  key_lens: device
- * int32 [B] or NULL.  All pointers are device pointers, 16-byte aligned.
+ * Layouts.  Q, K, V, O, dO, dQ, dK, dV: [B, H, N, d] with d innermost and
+ * contiguous, element type `dtype`; contiguous ([B, H, N, d] row-major) for
+ * every entry point except fa_fwd_strided and fa_bwd_strided, which take
+ * each tensor's batch, head and row strides (fa_strides), so that, e.g.,
+ * [B, N, H, d] memory or a fused QKV projection is read in place.  LSE:
+ * contiguous fp32 [B, H, N].  key_lens: device int32 [B] or NULL.  All
+ * pointers are device pointers, 16-byte aligned.
  *
  * Ownership.  The caller allocates and owns every buffer, including the
  * backward workspace.  The library never allocates or frees device memory,
@@ -49,12 +53,14 @@
  *   FA_ERR_INVALID_ARG  NULL or misaligned pointer, B/H/N <= 0, a size whose
  *                       element count overflows int64, non-finite or
  *                       non-positive scale, p outside [0, 1), workspace NULL
- *                       or smaller than fa_bwd_workspace_size().
+ *                       or smaller than fa_bwd_workspace_size(), an unknown
+ *                       dtype, strides that fa_strides rules out.
  *   FA_ERR_UNSUPPORTED  d not in {64, 128}; fp32 with dropout; fp32 backward;
- *                       one (b, h) slice of N * d elements of 2^32 bytes or
- *                       more (N >= 2^24 at d = 128, N >= 2^25 at d = 64 in
- *                       bf16): the kernels address a slice with 32-bit byte
- *                       offsets.
+ *                       one (b, h) slice whose N + 256 rows span 2^32 bytes
+ *                       or more (N >= 2^24 - 256 at d = 128, 2^25 - 256 at
+ *                       d = 64, for contiguous 16-bit rows): the kernels
+ *                       address a slice, including tiles fetched ahead past
+ *                       its end, with 32-bit byte offsets.
  *   FA_ERR_HIP          a launch failed (hipGetLastError after launching).
  * key_lens lives in device memory and cannot be range-checked on the host; the
  * kernels clamp each L_b into [0, N].
@@ -79,9 +85,31 @@ typedef enum {
 } fa_status;
 
 typedef enum {
-  FA_F32 = 0,  /* IEEE binary32 */
-  FA_BF16 = 1  /* bfloat16, round-to-nearest-even on output */
+  FA_F32 = 0,   /* IEEE binary32 */
+  FA_BF16 = 1,  /* bfloat16, round-to-nearest-even on output */
+  FA_F16 = 2    /* IEEE binary16, round-to-nearest-even on output */
 } fa_dtype;
+
+/*
+ * Element strides of one [B, H, N, d] tensor whose d elements per row are
+ * contiguous: element (b, h, n, e) is at base[b * batch + h * head + n * row
+ * + e] (in elements of the tensor's dtype, not bytes).  Contiguous
+ * [B, H, N, d] is {H * N * d, N * d, d}; [B, N, H, d] memory viewed as
+ * [B, H, N, d] is {N * H * d, d, H * d}.  Rules, checked on the host:
+ *   - row >= d, batch >= 0, head >= 0 (else FA_ERR_INVALID_ARG);
+ *   - batch, head and row are multiples of 16 bytes' worth of elements (8
+ *     for 16-bit types, 4 for fp32), so every row starts 16-byte aligned
+ *     (else FA_ERR_INVALID_ARG);
+ *   - outputs (O, dQ, dK, dV) give every (b, h, n) its own row: sorted by
+ *     stride, each dimension's stride is at least the span of the ones
+ *     inside it (else FA_ERR_INVALID_ARG);
+ *   - (N + 256) * row elements span fewer than 2^32 bytes (else
+ *     FA_ERR_UNSUPPORTED).
+ * Different tensors must not overlap (not checked).
+ */
+typedef struct {
+  int64_t batch, head, row;
+} fa_strides;
 
 /*
  * Forward pass: O and LSE.
@@ -96,7 +124,7 @@ typedef enum {
  *   dropout_p probability of dropping an element, 0 <= p < 1.
  *   seed      Philox key, used only when dropout_p > 0.
  *
- * dtype FA_BF16: d in {64, 128}, every mask and dropout combination.
+ * dtype FA_BF16, FA_F16: d in {64, 128}, every mask and dropout combination.
  * dtype FA_F32:  d in {64, 128}, causal mask and key_lens allowed, no
  *                dropout (FA_ERR_UNSUPPORTED).  A simple kernel meant for the
  *                small single-head fp32 workload, not tuned for large sizes.
@@ -107,14 +135,25 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  hipStream_t stream);
 
 /*
+ * fa_fwd on tensors laid out by strides: strides[0..3] are those of q, k, v
+ * and o (see fa_strides); NULL means all four contiguous.  LSE stays
+ * contiguous [B, H, N].  Same checks, kernels and results (bit for bit) as
+ * fa_fwd on the same values.
+ */
+fa_status fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const fa_strides* strides, int B, int H, int N, int d, fa_dtype dtype,
+                         float scale, int causal, const int32_t* key_lens, float dropout_p,
+                         uint64_t seed, hipStream_t stream);
+
+/*
  * Split-KV forward: fa_fwd's result for small B*H, where one workgroup per
  * query block would leave most of the GPU idle.  Each query block's key tiles
  * are split num_splits ways (FlashAttention-2's better work partitioning,
  * Flash Attention hardware-aware optimisation, section 4); every split runs
  * the online softmax over its share and writes its fp32 O and LSE to the
  * workspace, then a combine pass weights the splits by exp(LSE_s - LSE).
- * Same arguments, checks and mask/dropout semantics as fa_fwd (bf16 only:
- * FA_F32 is FA_ERR_UNSUPPORTED), plus
+ * Same arguments, checks and mask/dropout semantics as fa_fwd (bf16 and fp16
+ * only: FA_F32 is FA_ERR_UNSUPPORTED), plus
  *   num_splits       1 .. FA_MAX_SPLITS (else FA_ERR_INVALID_ARG); splits
  *                    that get no key tile are allowed and contribute nothing;
  *   workspace        device buffer of at least
@@ -150,7 +189,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype);
  *                     16-byte aligned; its contents on entry do not matter and
  *                     are garbage on exit.
  *
- * dtype FA_BF16 only (d in {64, 128}).  dQ, dK and dV are bitwise
+ * dtype FA_BF16 or FA_F16 (d in {64, 128}).  dQ, dK and dV are bitwise
  * deterministic: each is accumulated in fp32 registers by one workgroup and
  * written once (no atomics).
  */
@@ -159,6 +198,20 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
                  const int32_t* key_lens, float dropout_p, uint64_t seed,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_bwd on tensors laid out by strides: strides[0..7] are those of q, k, v,
+ * o, dout, dq, dk and dv (see fa_strides); NULL means all eight contiguous.
+ * lse stays contiguous [B, H, N]; the workspace is sized by
+ * fa_bwd_workspace_size as for fa_bwd.  Same checks, kernels and results (bit
+ * for bit) as fa_bwd on the same values.
+ */
+fa_status fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         const fa_strides* strides, int B, int H, int N, int d, fa_dtype dtype,
+                         float scale, int causal, const int32_t* key_lens, float dropout_p,
+                         uint64_t seed, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /*
  * The backward in stages.  fa_bwd enqueues fa_bwd_dq, then fa_bwd_dkdv, on its

@@ -8,10 +8,13 @@ V, O and the per-row log-sum-exp (no N x N matrix; ML Canon 48 FlashAttention,
 names of torch.nn.functional.scaled_dot_product_attention, the drop-in call the
 same page shows, for the cases the library computes.
 
-The kernels take contiguous [B, H, N, d] tensors.  layout="bnhd" accepts
-[B, N, H, d] (the layout of a fused QKV projection) and returns O in it; the
-tensors are then transposed into contiguous copies on the way in (and dO, dQ,
-dK, dV on the way through the backward), which costs one extra pass over each.
+The kernels take [B, H, N, d] tensors of any batch, head and row strides
+(last dimension contiguous, rows 16-byte aligned).  layout="bnhd" accepts
+[B, N, H, d] (the layout of a fused QKV projection) and returns O in it: the
+tensors go to the library as transposed views, O, dQ, dK and dV are
+allocated in the inputs' memory layout, and nothing is copied.  A tensor the
+strided entry points cannot address in place (e.g. an expanded gradient with
+zero strides) is copied to contiguous memory first.
 """
 
 import torch
@@ -19,11 +22,16 @@ import torch
 from . import binding
 
 
+def _in_place(t):
+    """t itself when the library can address it, else a contiguous copy."""
+    return t if binding.kernel_layout_ok(t) else t.contiguous()
+
+
 def _to_bhnd(t, layout):
     if layout == "bhnd":
-        return t.contiguous()
+        return _in_place(t)
     if layout == "bnhd":
-        return t.transpose(1, 2).contiguous()
+        return _in_place(t.transpose(1, 2))
     raise ValueError(f"layout must be 'bhnd' or 'bnhd', not {layout!r}")
 
 
@@ -34,8 +42,9 @@ def _from_bhnd(t, layout):
 def _splits(q, causal):
     """Key splits for the forward: 2 (fa_fwd_split) when the plain forward
     would launch fewer workgroups than the GPU has CUs (one per 128-query block,
-    causal ones in pairs), else 0 (fa_fwd).  bf16 on a GPU only."""
-    if q.dtype != torch.bfloat16 or not q.is_cuda:
+    causal ones in pairs), else 0 (fa_fwd).  16-bit types on a GPU, contiguous
+    tensors only (the split entry point takes no strides)."""
+    if q.dtype not in (torch.bfloat16, torch.float16) or not q.is_cuda or not q.is_contiguous():
         return 0
     B, H, N, _ = q.shape
     blocks = (N + 127) // 128
@@ -45,7 +54,7 @@ def _splits(q, causal):
 
 
 def _forward(q, k, v, scale, causal, key_lens, dropout_p, seed):
-    s = _splits(q, causal)
+    s = _splits(q, causal) if k.is_contiguous() and v.is_contiguous() else 0
     if s:
         return binding.forward_split(q, k, v, scale, causal, key_lens, dropout_p, seed, s)
     return binding.forward(q, k, v, scale, causal, key_lens, dropout_p, seed)
@@ -66,7 +75,7 @@ class FlashAttentionFunction(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
         scale, causal, dropout_p, seed = ctx.args
-        dq, dk, dv = binding.backward(q, k, v, o, do.contiguous(), lse, scale, causal,
+        dq, dk, dv = binding.backward(q, k, v, o, _in_place(do), lse, scale, causal,
                                       ctx.key_lens, dropout_p, seed)
         return dq, dk, dv, None, None, None, None, None
 
@@ -75,9 +84,9 @@ def flash_attention(q, k, v, scale=None, causal=False, key_lens=None, dropout_p=
                     layout="bhnd"):
     """Exact attention with autograd support.
 
-    q, k, v: bf16 CUDA tensors [B, H, N, d] (layout="bhnd") or [B, N, H, d]
-    (layout="bnhd"), d in {64, 128}; fp32 is accepted without autograd
-    (forward only).  scale defaults to 1/sqrt(d).  key_lens: int32 [B]
+    q, k, v: bf16 or fp16 CUDA tensors [B, H, N, d] (layout="bhnd") or
+    [B, N, H, d] (layout="bnhd"), d in {64, 128}, read in place; fp32 is
+    accepted without autograd (forward only).  scale defaults to 1/sqrt(d).  key_lens: int32 [B]
     (device or host) masking keys j >= key_lens[b].  dropout_p > 0 draws a
     Philox seed from torch's default CPU generator when seed is None; the same
     seed is replayed in the backward.

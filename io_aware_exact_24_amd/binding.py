@@ -1,10 +1,10 @@
 """ctypes binding of libfa.so with the C ABI's entry-point names.
 
 Argument marshalling only: torch tensors are checked for shape, dtype, device
-and contiguity, then passed as raw device pointers together with the HIP
-stream handle of torch's current stream.  All compute happens in the
-library's kernels.  If libfa.so is missing the first call raises; there is no
-fallback.
+and layout, then passed as raw device pointers (and, for the strided entry
+points, their element strides) together with the HIP stream handle of torch's
+current stream.  All compute happens in the library's kernels.  If libfa.so
+is missing the first call raises; there is no fallback.
 """
 
 import ctypes
@@ -14,15 +14,20 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libfa.so"
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
-FA_F32, FA_BF16 = 0, 1
+FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_split", "fa_fwd_split_workspace_size",
-           "fa_bwd_noalloc")
+           "fa_bwd_noalloc", "fa_fwd_strided", "fa_bwd_strided")
 FA_MAX_SPLITS = 64
 FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
+
+
+class FaStrides(ctypes.Structure):
+    """fa_strides: element strides (batch, head, row) of a [B, H, N, d] tensor."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("row", ctypes.c_int64)]
 
 
 class FaError(RuntimeError):
@@ -68,6 +73,12 @@ def load_library():
     lib.fa_bwd_noalloc.restype = i
     lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f,
                                    u64, vp]
+    sp = ctypes.POINTER(FaStrides)
+    lib.fa_fwd_strided.restype = i
+    lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, sp, i, i, i, i, i, f, i, vp, f, u64, vp]
+    lib.fa_bwd_strided.restype = i
+    lib.fa_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sp, i, i, i, i, i, f, i, vp,
+                                   f, u64, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -81,6 +92,8 @@ def _dtype_code(t):
 
     if t.dtype == torch.bfloat16:
         return FA_BF16
+    if t.dtype == torch.float16:
+        return FA_F16
     if t.dtype == torch.float32:
         return FA_F32
     raise TypeError(f"unsupported dtype {t.dtype}")
@@ -94,6 +107,34 @@ def _check(t, shape, dtype, device, name):
     if t.shape != shape or t.dtype != dtype or t.device != device or not t.is_contiguous():
         raise ValueError(f"{name}: expected contiguous {tuple(shape)} {dtype} on {device}, got "
                          f"{tuple(t.shape)} {t.dtype} on {t.device} (contiguous={t.is_contiguous()})")
+
+
+def _check_view(t, shape, dtype, device, name):
+    """A [B, H, N, d] tensor of any strides whose last dimension is contiguous
+    (the library checks the strides themselves)."""
+    if t.shape != shape or t.dtype != dtype or t.device != device or (t.shape[-1] > 1 and
+                                                                         t.stride(-1) != 1):
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype} on {device} with a contiguous "
+                         f"last dimension, got {tuple(t.shape)} {t.dtype} on {t.device} strides "
+                         f"{t.stride()}")
+
+
+def _strides(tensors):
+    arr = (FaStrides * len(tensors))()
+    for a, t in zip(arr, tensors):
+        a.batch, a.head, a.row = t.stride(0), t.stride(1), t.stride(2)
+    return arr
+
+
+def kernel_layout_ok(t):
+    """True when the strided entry points can read or write t in place: last
+    dimension contiguous, 16-byte aligned base and strides, rows at least d
+    elements apart (fa_strides in include/fa.h)."""
+    if t.dim() != 4 or t.stride(-1) != 1 or t.data_ptr() % 16 != 0:
+        return False
+    unit = 16 // t.element_size()
+    d = t.shape[-1]
+    return all(s >= 0 and s % unit == 0 for s in t.stride()[:3]) and t.stride(2) >= d
 
 
 def _stream(stream, device):
@@ -130,6 +171,26 @@ def fa_fwd(q, k, v, o, lse, scale, causal=False, key_lens=None, dropout_p=0.0, s
                     _stream(stream, q.device))
     if st != FA_OK:
         raise FaError(st, "fa_fwd")
+
+
+def fa_fwd_strided(q, k, v, o, lse, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
+                   stream=None):
+    """fa_fwd on [B, H, N, d] views of any strides (last dimension
+    contiguous): each tensor's batch, head and row strides go to the library,
+    nothing is copied."""
+    import torch
+
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_view(t, q.shape, q.dtype, q.device, name)
+    _check(lse, (B, H, N), torch.float32, q.device, "lse")
+    kl = _key_lens(key_lens, B, q.device)
+    st = lib.fa_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _strides((q, k, v, o)),
+                            B, H, N, d, _dtype_code(q), float(scale), int(bool(causal)), _ptr(kl),
+                            float(dropout_p), int(seed), _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_strided")
 
 
 def fa_fwd_split_workspace_size(B, H, N, d, num_splits, dtype_code=FA_BF16):
@@ -199,6 +260,30 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None
                     _stream(stream, q.device))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None,
+                   dropout_p=0.0, seed=0, workspace=None, stream=None):
+    """fa_bwd on [B, H, N, d] views of any strides (last dimension
+    contiguous); nothing is copied."""
+    import torch
+
+    lib = load_library()
+    B, H, N, d = q.shape
+    ts = (q, k, v, o, dout, dq, dk, dv)
+    for name, t in zip(("q", "k", "v", "o", "dout", "dq", "dk", "dv"), ts):
+        _check_view(t, q.shape, q.dtype, q.device, name)
+    _check(lse, (B, H, N), torch.float32, q.device, "lse")
+    kl = _key_lens(key_lens, B, q.device)
+    if workspace is None:
+        raise ValueError("fa_bwd_strided needs a workspace tensor (see fa_bwd_workspace_size)")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_bwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                            _ptr(dk), _ptr(dv), _strides(ts), B, H, N, d, _dtype_code(q),
+                            float(scale), int(bool(causal)), _ptr(kl), float(dropout_p), int(seed),
+                            _ptr(workspace), ws_bytes, _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_strided")
 
 
 def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None,
@@ -275,26 +360,36 @@ def fa_bwd_dq(q, k, v, o, dout, lse, dq, scale, causal=False, key_lens=None, dro
 
 
 def forward(q, k, v, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0, stream=None):
-    """Allocate O and LSE with torch and call fa_fwd."""
+    """Allocate O (in q's memory layout) and LSE with torch and call fa_fwd, or
+    fa_fwd_strided when a tensor is not contiguous [B, H, N, d]."""
     import torch
 
     B, H, N, d = q.shape
-    o = torch.empty_like(q)
+    o = torch.empty_like(q)  # keeps q's strides for a dense q
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_fwd(q, k, v, o, lse, scale, causal, key_lens, dropout_p, seed, stream)
+    if all(t.is_contiguous() for t in (q, k, v, o)):
+        fa_fwd(q, k, v, o, lse, scale, causal, key_lens, dropout_p, seed, stream)
+    else:
+        fa_fwd_strided(q, k, v, o, lse, scale, causal, key_lens, dropout_p, seed, stream)
     return o, lse
 
 
 def backward(q, k, v, o, dout, lse, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
              stream=None, workspace=None):
-    """Allocate dQ, dK, dV (and the workspace unless given) and call fa_bwd."""
+    """Allocate dQ, dK, dV (each in its input's memory layout; the workspace
+    unless given) and call fa_bwd, or fa_bwd_strided when a tensor is not
+    contiguous [B, H, N, d]."""
     import torch
 
     B, H, N, d = q.shape
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
         nbytes = fa_bwd_workspace_size(B, H, N, d, _dtype_code(q))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, key_lens, dropout_p, seed,
-           workspace, stream)
+    if all(t.is_contiguous() for t in (q, k, v, o, dout, dq, dk, dv)):
+        fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, key_lens, dropout_p, seed,
+               workspace, stream)
+    else:
+        fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, key_lens, dropout_p, seed,
+                       workspace, stream)
     return dq, dk, dv

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <initializer_list>
 #include <mutex>
 
@@ -25,13 +26,51 @@ int64_t elems(int B, int H, int N, int d) {
   return n;
 }
 
+bool valid_dtype(fa_dtype t) { return t == FA_F32 || t == FA_BF16 || t == FA_F16; }
+bool is16(fa_dtype t) { return t == FA_BF16 || t == FA_F16; }
+uint64_t elem_bytes(fa_dtype t) { return t == FA_F32 ? 4 : 2; }
+
 // The kernels address one (b, h) slice of a tensor through a buffer resource
 // whose byte range, and every tile offset inside it (rows up to 256 past the
 // last, for tiles fetched ahead), is a 32-bit number: (N + 256) rows of
 // `row_stride` elements must span fewer than 2^32 bytes.
 bool head_bytes_fit(int N, int64_t row_stride, fa_dtype dtype) {
-  const uint64_t elem = dtype == FA_F32 ? 4 : 2;
-  return ((uint64_t)N + 256) * (uint64_t)row_stride * elem <= (1ull << 32);
+  return ((uint64_t)N + 256) * (uint64_t)row_stride * elem_bytes(dtype) <= (1ull << 32);
+}
+
+// The fa_strides rules of fa.h for one tensor (`output`: it is written).
+fa_status check_strides(const fa_strides& s, int B, int H, int N, int d, fa_dtype dtype,
+                        bool output) {
+  const int64_t unit = 16 / (int64_t)elem_bytes(dtype);  // elements per 16 bytes
+  if (s.batch < 0 || s.head < 0 || s.row < d) return FA_ERR_INVALID_ARG;
+  if (s.batch % unit != 0 || s.head % unit != 0 || s.row % unit != 0) return FA_ERR_INVALID_ARG;
+  // The largest element offset, (B-1) batch + (H-1) head + (N-1) row + d - 1,
+  // must fit int64: each product is kept at most 2^61, so the sum stays below
+  // 2^63.
+  const int64_t lim = INT64_MAX / 4;
+  if (s.batch > lim / B || s.head > lim / H || s.row > lim / N) return FA_ERR_INVALID_ARG;
+  if (output) {
+    // Every (b, h, n) owns its own row: sorted by stride (dimensions of
+    // extent 1 do not matter), each stride is at least the span of the
+    // dimensions inside it, the innermost span being the d elements of a row.
+    struct Dim {
+      int64_t stride, extent;
+    } dims[3] = {{s.batch, B}, {s.head, H}, {s.row, N}};
+    std::sort(dims, dims + 3, [](const Dim& a, const Dim& b) { return a.stride < b.stride; });
+    int64_t span = d;
+    for (const Dim& dm : dims) {
+      if (dm.extent == 1) continue;
+      if (dm.stride < span) return FA_ERR_INVALID_ARG;
+      span = dm.stride * (dm.extent - 1) + span;
+    }
+  }
+  if (!head_bytes_fit(N, s.row, dtype)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+fa::Strides to_strides(const fa_strides* s, int H, int N, int d) {
+  if (s == nullptr) return fa::contiguous_bhnd(H, N, d);
+  return fa::Strides{s->batch, s->head, s->row};
 }
 
 bool valid_dropout(float p) { return isfinite(p) && p >= 0.0f && p < 1.0f; }
@@ -52,22 +91,30 @@ size_t pad256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // fa_fwd (num_splits 0) and fa_fwd_split (num_splits >= 1, bf16 only, with a
 // workspace of fa_fwd_split_workspace_size bytes): checks, then the launch.
-fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                  int N, int d, fa_dtype dtype, float scale, int causal, const int32_t* key_lens,
-                  float dropout_p, uint64_t seed, int num_splits, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream) {
+// strides: q, k, v, o (NULL: contiguous).
+fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const fa_strides* strides, int B, int H, int N, int d, fa_dtype dtype,
+                  float scale, int causal, const int32_t* key_lens, float dropout_p, uint64_t seed,
+                  int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
   if (key_lens != nullptr && ((uintptr_t)key_lens & 3u) != 0) return FA_ERR_INVALID_ARG;
   if (elems(B, H, N, d) < 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale <= 0.0f) return FA_ERR_INVALID_ARG;
   if (!valid_dropout(dropout_p)) return FA_ERR_INVALID_ARG;
-  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (!head_bytes_fit(N, d, dtype)) return FA_ERR_UNSUPPORTED;
+  if (strides != nullptr) {
+    for (int t = 0; t < 4; ++t) {
+      const fa_status st = check_strides(strides[t], B, H, N, d, dtype, t == 3);
+      if (st != FA_OK) return st;
+    }
+  } else if (!head_bytes_fit(N, d, dtype)) {
+    return FA_ERR_UNSUPPORTED;
+  }
   if (dtype == FA_F32 && dropout_p > 0.0f) return FA_ERR_UNSUPPORTED;
   if (num_splits > 0) {
-    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!is16(dtype)) return FA_ERR_UNSUPPORTED;
     if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
     if (workspace_bytes < fa_fwd_split_workspace_size(B, H, N, d, dtype, num_splits))
       return FA_ERR_INVALID_ARG;
@@ -79,7 +126,11 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   a.v = v;
   a.o = o;
   a.lse = lse;
-  a.sq = a.sk = a.sv = a.so = fa::contiguous_bhnd(H, N, d);
+  a.fp16 = dtype == FA_F16;
+  a.sq = to_strides(strides ? &strides[0] : nullptr, H, N, d);
+  a.sk = to_strides(strides ? &strides[1] : nullptr, H, N, d);
+  a.sv = to_strides(strides ? &strides[2] : nullptr, H, N, d);
+  a.so = to_strides(strides ? &strides[3] : nullptr, H, N, d);
   a.B = B;
   a.H = H;
   a.N = N;
@@ -97,7 +148,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     a.opart = (float*)workspace;
     a.lsepart = (float*)((char*)workspace + pad256((size_t)num_splits * rows * d * 4));
   }
-  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_16(a, stream) : fa::launch_fwd_f32(a, stream);
+  const hipError_t e = is16(dtype) ? fa::launch_fwd_16(a, stream) : fa::launch_fwd_f32(a, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -119,12 +170,20 @@ const char* fa_status_string(fa_status s) {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, fa_dtype dtype, float scale, int causal, const int32_t* key_lens,
                  float dropout_p, uint64_t seed, hipStream_t stream) {
-  return run_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, key_lens, dropout_p, seed, 0,
-                 nullptr, 0, stream);
+  return run_fwd(q, k, v, o, lse, nullptr, B, H, N, d, dtype, scale, causal, key_lens, dropout_p,
+                 seed, 0, nullptr, 0, stream);
+}
+
+fa_status fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const fa_strides* strides, int B, int H, int N, int d, fa_dtype dtype,
+                         float scale, int causal, const int32_t* key_lens, float dropout_p,
+                         uint64_t seed, hipStream_t stream) {
+  return run_fwd(q, k, v, o, lse, strides, B, H, N, d, dtype, scale, causal, key_lens, dropout_p,
+                 seed, 0, nullptr, 0, stream);
 }
 
 size_t fa_fwd_split_workspace_size(int B, int H, int N, int d, fa_dtype dtype, int num_splits) {
-  if (elems(B, H, N, d) < 0 || (d != 64 && d != 128) || dtype != FA_BF16 || num_splits < 1 ||
+  if (elems(B, H, N, d) < 0 || (d != 64 && d != 128) || !is16(dtype) || num_splits < 1 ||
       num_splits > FA_MAX_SPLITS || !head_bytes_fit(N, d, dtype))
     return 0;
   const size_t rows = (size_t)B * H * N;
@@ -136,12 +195,12 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        const int32_t* key_lens, float dropout_p, uint64_t seed, int num_splits,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_INVALID_ARG;
-  return run_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, key_lens, dropout_p, seed,
-                 num_splits, workspace, workspace_bytes, stream);
+  return run_fwd(q, k, v, o, lse, nullptr, B, H, N, d, dtype, scale, causal, key_lens, dropout_p,
+                 seed, num_splits, workspace, workspace_bytes, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype) {
-  if (dtype != FA_BF16 || (d != 64 && d != 128)) return 0;
+  if (!is16(dtype) || (d != 64 && d != 128)) return 0;
   if (elems(B, H, N, d) < 0 || !head_bytes_fit(N, d, dtype)) return 0;
   return 2 * row_array_bytes(B, H, N);
 }
@@ -162,19 +221,22 @@ fa_status check_bwd(std::initializer_list<const void*> ptrs, const int32_t* key_
   if (elems(B, H, N, d) < 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale <= 0.0f) return FA_ERR_INVALID_ARG;
   if (!valid_dropout(dropout_p)) return FA_ERR_INVALID_ARG;
-  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!is16(dtype)) return FA_ERR_UNSUPPORTED;
   if (!head_bytes_fit(N, d, dtype)) return FA_ERR_UNSUPPORTED;
   if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d, dtype)) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 
+// strides: q, k, v, o, dout, dq, dk, dv (NULL: contiguous).
 fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                  float scale, int causal, const int32_t* key_lens, float dropout_p, uint64_t seed,
-                  void* workspace, int stages, hipStream_t stream) {
+                  const float* lse, void* dq, void* dk, void* dv, const fa_strides* strides, int B,
+                  int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                  const int32_t* key_lens, float dropout_p, uint64_t seed, void* workspace,
+                  int stages, hipStream_t stream) {
   fa::BwdArgs a;
+  a.fp16 = dtype == FA_F16;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -198,7 +260,8 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   // workspace: D, then LSE * log2(e)
   a.delta = (float*)workspace;
   a.lse2 = (float*)((char*)workspace + row_array_bytes(B, H, N));
-  a.sq = a.sk = a.sv = a.so = a.sdo = a.sdq = a.sdk = a.sdv = fa::contiguous_bhnd(H, N, d);
+  fa::Strides* dst[8] = {&a.sq, &a.sk, &a.sv, &a.so, &a.sdo, &a.sdq, &a.sdk, &a.sdv};
+  for (int t = 0; t < 8; ++t) *dst[t] = to_strides(strides ? &strides[t] : nullptr, H, N, d);
   const hipError_t e = fa::launch_bwd_16(a, stages, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -216,8 +279,29 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   const fa_status st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, key_lens, B, H, N, d, dtype,
                                  scale, dropout_p, workspace, workspace_bytes);
   if (st != FA_OK) return st;
-  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens, dropout_p,
-                 seed, workspace, fa::kBwdAll, stream);
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, nullptr, B, H, N, d, dtype, scale, causal,
+                 key_lens, dropout_p, seed, workspace, fa::kBwdAll, stream);
+}
+
+fa_status fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         const fa_strides* strides, int B, int H, int N, int d, fa_dtype dtype,
+                         float scale, int causal, const int32_t* key_lens, float dropout_p,
+                         uint64_t seed, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  // The strides first (after what they depend on), then every check of fa_bwd.
+  if (elems(B, H, N, d) < 0 || !valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
+  if (strides != nullptr) {
+    for (int t = 0; t < 8; ++t) {
+      const fa_status st = check_strides(strides[t], B, H, N, d, dtype, t >= 5);
+      if (st != FA_OK) return st;
+    }
+  }
+  const fa_status st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, key_lens, B, H, N, d, dtype,
+                                 scale, dropout_p, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, strides, B, H, N, d, dtype, scale, causal,
+                 key_lens, dropout_p, seed, workspace, fa::kBwdAll, stream);
 }
 
 fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N,
@@ -226,8 +310,8 @@ fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse, i
   const fa_status st = check_bwd({o, dout, lse}, nullptr, B, H, N, d, dtype, 1.0f, 0.0f, workspace,
                                  workspace_bytes);
   if (st != FA_OK) return st;
-  return run_bwd(kUnused, kUnused, kUnused, o, dout, lse, nullptr, nullptr, nullptr, B, H, N, d,
-                 1.0f, 0, nullptr, 0.0f, 0, workspace, fa::kBwdPre, stream);
+  return run_bwd(kUnused, kUnused, kUnused, o, dout, lse, nullptr, nullptr, nullptr, nullptr, B, H, N,
+                 d, dtype, 1.0f, 0, nullptr, 0.0f, 0, workspace, fa::kBwdPre, stream);
 }
 
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
@@ -237,8 +321,9 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* d
   const fa_status st = check_bwd({q, k, v, dout, dk, dv}, key_lens, B, H, N, d, dtype, scale,
                                  dropout_p, workspace, workspace_bytes);
   if (st != FA_OK) return st;
-  return run_bwd(q, k, v, kUnused, dout, (const float*)kUnused, nullptr, dk, dv, B, H, N, d, scale,
-                 causal, key_lens, dropout_p, seed, (void*)workspace, fa::kBwdKV, stream);
+  return run_bwd(q, k, v, kUnused, dout, (const float*)kUnused, nullptr, dk, dv, nullptr, B, H, N, d,
+                 dtype, scale, causal, key_lens, dropout_p, seed, (void*)workspace, fa::kBwdKV,
+                 stream);
 }
 
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -248,8 +333,8 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, 
   const fa_status st = check_bwd({q, k, v, o, dout, lse, dq}, key_lens, B, H, N, d, dtype, scale,
                                  dropout_p, workspace, workspace_bytes);
   if (st != FA_OK) return st;
-  return run_bwd(q, k, v, o, dout, lse, dq, nullptr, nullptr, B, H, N, d, scale, causal, key_lens,
-                 dropout_p, seed, workspace, fa::kBwdQ, stream);
+  return run_bwd(q, k, v, o, dout, lse, dq, nullptr, nullptr, nullptr, B, H, N, d, dtype, scale,
+                 causal, key_lens, dropout_p, seed, workspace, fa::kBwdQ, stream);
 }
 
 }  // extern "C"
@@ -322,8 +407,8 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void
   if (st != FA_OK) return st;
   // The dQ stage writes D and LSE * log2(e) for every row before the dK/dV
   // stage reads them (same stream), so nothing needs clearing.
-  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens, dropout_p,
-                 seed, ws, fa::kBwdAll, stream);
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, nullptr, B, H, N, d, dtype, scale, causal,
+                 key_lens, dropout_p, seed, ws, fa::kBwdAll, stream);
 }
 
 }  // extern "C"

@@ -235,3 +235,108 @@ def test_noalloc_limit_is_the_workspace_of_4m_rows(lib):
         binding.FA_NOALLOC_SCRATCH_BYTES
     assert lib.fa_bwd_workspace_size(1, 1, (1 << 22) + 1, 64, binding.FA_BF16) > \
         binding.FA_NOALLOC_SCRATCH_BYTES
+
+
+# ---- fa_fwd_strided / fa_bwd_strided: the fa_strides rules of include/fa.h
+#
+# No call here may pass every check: it would launch kernels on the dummy
+# pointers.  Strides that are accepted are shown with a later check failing
+# instead (fp32 with dropout in the forward, fp32 in the backward: both are
+# UNSUPPORTED only once the strides have passed).
+
+
+def contig(H, N, d):
+    return (H * N * d, N * d, d)
+
+
+def strides_arr(rows):
+    arr = (binding.FaStrides * len(rows))()
+    for a, (b, h, n) in zip(arr, rows):
+        a.batch, a.head, a.row = b, h, n
+    return arr
+
+
+def fwd_s(lib, rows, B=2, H=2, N=128, d=64, dtype=binding.FA_BF16, p=0.0):
+    return lib.fa_fwd_strided(*([P] * 5), strides_arr(rows), B, H, N, d, dtype, 0.125, 0, None, p, 0,
+                              None)
+
+
+def fwd_s_accepts(lib, rows, **kw):
+    """The strides pass (fp32 + dropout is then the first check to fail)."""
+    return fwd_s(lib, rows, dtype=binding.FA_F32, p=0.1, **kw) == UNSUPPORTED
+
+
+def bwd_s(lib, rows, B=2, H=2, N=128, d=64, dtype=binding.FA_BF16):
+    ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d, binding.FA_BF16)
+    return lib.fa_bwd_strided(*([P] * 9), strides_arr(rows), B, H, N, d, dtype, 0.125, 0, None, 0.0,
+                              0, P, ws_bytes, None)
+
+
+def bwd_s_accepts(lib, rows):
+    """The strides pass (the fp32 backward is then the first check to fail)."""
+    return bwd_s(lib, rows, dtype=binding.FA_F32) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("which", range(4))
+@pytest.mark.parametrize("bad,expect", [
+    ((0, 0, 32), INVALID),                 # row < d
+    ((-64, 64, 64), INVALID),              # negative batch stride
+    ((2 * 128 * 64, 128 * 64, 68), INVALID),  # row not a multiple of 8 bf16 elements
+    ((2 * 128 * 64 + 4, 128 * 64, 64), INVALID),  # batch not 16-byte aligned
+    ((2 * 128 * 64, 128 * 64, 1 << 23), UNSUPPORTED),  # (N + 256) rows span > 2^32 bytes
+])
+def test_strided_forward_rejects_bad_strides(lib, which, bad, expect):
+    rows = [contig(2, 128, 64)] * 4
+    assert fwd_s_accepts(lib, rows)
+    rows[which] = bad
+    assert fwd_s(lib, rows) == expect
+
+
+def test_strided_output_rows_must_not_overlap(lib):
+    good = contig(2, 128, 64)
+    # o with head stride 0: two heads would write the same rows
+    assert fwd_s(lib, [good] * 3 + [(2 * 128 * 64, 0, 64)]) == INVALID
+    # o rows 64 apart but heads only 64 * 100 apart: head 1 overlaps rows 100.. of head 0
+    assert fwd_s(lib, [good] * 3 + [(2 * 128 * 64, 64 * 100, 64)]) == INVALID
+    # [B, N, H, d] memory (rows H * d apart, heads d apart) is a valid output,
+    # and so are rows with gaps between them
+    bnhd = (128 * 2 * 64, 64, 2 * 64)
+    assert fwd_s_accepts(lib, [good] * 3 + [bnhd])
+    assert fwd_s_accepts(lib, [good] * 3 + [(2 * 128 * 72, 128 * 72, 72)])
+    # an input may repeat rows (head stride 0): only outputs must be one-to-one
+    assert fwd_s_accepts(lib, [good, (2 * 128 * 64, 0, 64), good, good])
+
+
+@pytest.mark.parametrize("which,expect", [(0, INVALID), (4, INVALID), (5, INVALID), (7, INVALID)])
+def test_strided_backward_rejects_bad_strides(lib, which, expect):
+    rows = [contig(2, 128, 64)] * 8
+    assert bwd_s_accepts(lib, rows)
+    rows[which] = (0, 0, 32)
+    assert bwd_s(lib, rows) == expect
+
+
+def test_strided_backward_outputs_must_not_overlap(lib):
+    rows = [contig(2, 128, 64)] * 8
+    rows[6] = (0, 128 * 64, 64)  # dk: both batch entries on the same rows
+    assert bwd_s(lib, rows) == INVALID
+    rows[6] = contig(2, 128, 64)
+    rows[1] = (0, 128 * 64, 64)  # k: an input may be shared across the batch
+    assert bwd_s_accepts(lib, rows)
+
+
+def test_fp16_is_a_16_bit_type_everywhere(lib):
+    f16 = binding.FA_F16
+    assert fwd(lib, dtype=f16, d=96) == UNSUPPORTED   # recognised, d still checked
+    assert fwd(lib, dtype=f16, p=1.0) == INVALID
+    assert fwd(lib, dtype=3) == INVALID
+    assert lib.fa_bwd_workspace_size(1, 1, 128, 64, f16) == \
+        lib.fa_bwd_workspace_size(1, 1, 128, 64, binding.FA_BF16)
+    assert lib.fa_fwd_split_workspace_size(1, 1, 128, 64, f16, 2) == \
+        lib.fa_fwd_split_workspace_size(1, 1, 128, 64, binding.FA_BF16, 2)
+    assert bwd(lib, dtype=f16, d=96) == UNSUPPORTED
+    # fp16 rows of 16 bytes: strides in units of 8 elements, like bf16
+    rows = [contig(2, 128, 64)] * 4
+    rows[0] = (2 * 128 * 64, 128 * 64, 68)
+    assert fwd_s(lib, rows, dtype=f16) == INVALID
+    # fp32 rows: units of 4 elements
+    assert fwd_s_accepts(lib, rows)
