@@ -40,8 +40,12 @@ def flops(B, H, N, d, causal):
     return f, 2.5 * f
 
 
-KERNEL_SOURCES = {"fwd_bf16_kernel": "fa_fwd.hip", "bwd_dkdv_kernel": "fa_bwd.hip",
-                  "bwd_dq_kernel": "fa_bwd.hip", "bwd_pre_kernel": "fa_bwd.hip"}
+# The source files that define each kernel (besides the headers every kernel
+# includes).
+KERNEL_SOURCES = {"fwd_kernel": ("fa_fwd.hip",),
+                  "bwd_dkdv_kernel": ("fa_bwd_kernels.hpp", "fa_bwd_dkdv.hip"),
+                  "bwd_dq_kernel": ("fa_bwd_kernels.hpp", "fa_bwd_dq.hip"),
+                  "bwd_pre_kernel": ("fa_bwd_kernels.hpp", "fa_bwd_dq.hip")}
 
 
 def source_digest(kernel):
@@ -49,7 +53,7 @@ def source_digest(kernel):
     kernel includes: it changes whenever that kernel's code can have changed."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "io_aware_exact_24_amd", "csrc")
-    for name in (KERNEL_SOURCES[kernel], "fa_common.hpp", "fa_internal.hpp"):
+    for name in KERNEL_SOURCES[kernel] + ("fa_common.hpp", "fa_internal.hpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -406,7 +410,7 @@ def main():
     # N x N x d products per (query, key) pair, the dK/dV kernel four, the dQ
     # kernel three (fb is five).
     kflops = {"fwd": ff, "bwd_dkdv": fb * 4 / 5, "bwd_dq": fb * 3 / 5}
-    kernel_names = {"fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
+    kernel_names = {"fwd": "fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
     dom = max(kflops, key=lambda n: per[n])
     achieved = kflops[dom] / (per[dom] * 1e-3) / 1e12
     roofline = {

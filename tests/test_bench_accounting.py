@@ -32,10 +32,10 @@ def test_stored_traffic_follows_the_kernel_digest(tmp_path, monkeypatch):
         "| kernel | source digest | read (MiB) | written (MiB) | total bytes per launch |\n"
         "|---|---|---|---|---|\n"
         f"| `bwd_dkdv_kernel` | `{good}` | 500.0 | 250.0 | 7.8643e+08 |\n"
-        f"| `fwd_bf16_kernel` | `{stale}` | 400.0 | 130.0 | 5.5574e+08 |\n")
+        f"| `fwd_kernel` | `{stale}` | 400.0 | 130.0 | 5.5574e+08 |\n")
     digests = {k: bench.source_digest(k) for k in bench.KERNEL_SOURCES}
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))  # the summary file read from here
     monkeypatch.setattr(bench, "source_digest", digests.__getitem__)  # sources as they are
     assert bench.stored_traffic("bwd_dkdv_kernel") == pytest.approx(7.8643e8)
-    assert bench.stored_traffic("fwd_bf16_kernel") is None  # sources changed since
+    assert bench.stored_traffic("fwd_kernel") is None  # sources changed since
     assert bench.stored_traffic("bwd_dq_kernel") is None    # no row
