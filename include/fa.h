@@ -55,7 +55,8 @@
  *                       non-positive scale, p outside [0, 1), workspace NULL
  *                       or smaller than fa_bwd_workspace_size(), an unknown
  *                       dtype, strides that fa_strides rules out.
- *   FA_ERR_UNSUPPORTED  d not in {64, 128}; fp32 with dropout; fp32 backward;
+ *   FA_ERR_UNSUPPORTED  d not in {32, 64, 96, 128, 256}; fp32 with dropout;
+ *                       the split forward outside 16-bit d in {64, 128};
  *                       one (b, h) slice whose N + 256 rows span 2^32 bytes
  *                       or more (N >= 2^24 - 256 at d = 128, 2^25 - 256 at
  *                       d = 64, for contiguous 16-bit rows): the kernels
@@ -124,10 +125,14 @@ typedef struct {
  *   dropout_p probability of dropping an element, 0 <= p < 1.
  *   seed      Philox key, used only when dropout_p > 0.
  *
- * dtype FA_BF16, FA_F16: d in {64, 128}, every mask and dropout combination.
- * dtype FA_F32:  d in {64, 128}, causal mask and key_lens allowed, no
- *                dropout (FA_ERR_UNSUPPORTED).  A simple kernel meant for the
- *                small single-head fp32 workload, not tuned for large sizes.
+ * Head sizes and kernels:
+ *   FA_BF16, FA_F16 at d in {64, 128}: the MFMA kernels, every mask and
+ *     dropout combination.
+ *   FA_BF16, FA_F16 at d in {32, 96, 256}, and FA_F32 at every d in
+ *     {32, 64, 96, 128, 256}: generic kernels (fp32 arithmetic on the vector
+ *     ALUs, 32-row tiles in LDS; correct, not tuned).  FA_F32 takes no
+ *     dropout (FA_ERR_UNSUPPORTED); its forward at d in {64, 128} is a
+ *     one-thread-per-query kernel meant for the small single-head workload.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
@@ -153,7 +158,7 @@ fa_status fa_fwd_strided(const void* q, const void* k, const void* v, void* o, f
  * the online softmax over its share and writes its fp32 O and LSE to the
  * workspace, then a combine pass weights the splits by exp(LSE_s - LSE).
  * Same arguments, checks and mask/dropout semantics as fa_fwd (bf16 and fp16
- * only: FA_F32 is FA_ERR_UNSUPPORTED), plus
+ * at d in {64, 128} only, else FA_ERR_UNSUPPORTED), plus
  *   num_splits       1 .. FA_MAX_SPLITS (else FA_ERR_INVALID_ARG); splits
  *                    that get no key tile are allowed and contribute nothing;
  *   workspace        device buffer of at least
@@ -189,9 +194,10 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype);
  *                     16-byte aligned; its contents on entry do not matter and
  *                     are garbage on exit.
  *
- * dtype FA_BF16 or FA_F16 (d in {64, 128}).  dQ, dK and dV are bitwise
- * deterministic: each is accumulated in fp32 registers by one workgroup and
- * written once (no atomics).
+ * Every dtype and head size of fa_fwd (the MFMA kernels for 16-bit d in
+ * {64, 128}, the generic kernels otherwise; fp32 without dropout).  dQ, dK
+ * and dV are bitwise deterministic: each is accumulated in fp32 registers by
+ * one workgroup and written once (no atomics).
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse, void* dq, void* dk, void* dv,

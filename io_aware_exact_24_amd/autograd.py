@@ -84,9 +84,10 @@ def flash_attention(q, k, v, scale=None, causal=False, key_lens=None, dropout_p=
                     layout="bhnd"):
     """Exact attention with autograd support.
 
-    q, k, v: bf16 or fp16 CUDA tensors [B, H, N, d] (layout="bhnd") or
-    [B, N, H, d] (layout="bnhd"), d in {64, 128}, read in place; fp32 is
-    accepted without autograd (forward only).  scale defaults to 1/sqrt(d).  key_lens: int32 [B]
+    q, k, v: bf16, fp16 or fp32 CUDA tensors [B, H, N, d] (layout="bhnd") or
+    [B, N, H, d] (layout="bnhd"), d in {32, 64, 96, 128, 256}, read in place
+    (16-bit d = 64 and 128 run on the MFMA kernels, the rest on the generic
+    ones; fp32 takes no dropout).  scale defaults to 1/sqrt(d).  key_lens: int32 [B]
     (device or host) masking keys j >= key_lens[b].  dropout_p > 0 draws a
     Philox seed from torch's default CPU generator when seed is None; the same
     seed is replayed in the backward.

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["fa_fwd.hip", "fa_bwd_dkdv.hip", "fa_bwd_dq.hip", "fa_bwd.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd_dkdv.hip", "fa_bwd_dq.hip", "fa_bwd.hip", "fa_generic.hip",
+           "fa_api.cpp"]
 # The dK/dV kernel keeps its long-lived accumulators in AccVGPRs through inline
 # assembly; every other MFMA must write ordinary VGPRs, which the VALU reads.
 _VGPR_FORM = ["-mllvm", "--amdgpu-mfma-vgpr-form"]

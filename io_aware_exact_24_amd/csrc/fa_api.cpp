@@ -28,6 +28,9 @@ int64_t elems(int B, int H, int N, int d) {
 
 bool valid_dtype(fa_dtype t) { return t == FA_F32 || t == FA_BF16 || t == FA_F16; }
 bool is16(fa_dtype t) { return t == FA_BF16 || t == FA_F16; }
+// The MFMA kernels: 16-bit types at d = 64 and 128.  Every other supported
+// combination runs on the generic kernels.
+bool mfma_path(fa_dtype t, int d) { return is16(t) && (d == 64 || d == 128); }
 uint64_t elem_bytes(fa_dtype t) { return t == FA_F32 ? 4 : 2; }
 
 // The kernels address one (b, h) slice of a tensor through a buffer resource
@@ -103,7 +106,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (!isfinite(scale) || scale <= 0.0f) return FA_ERR_INVALID_ARG;
   if (!valid_dropout(dropout_p)) return FA_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!fa::generic_head_size(d)) return FA_ERR_UNSUPPORTED;
   if (strides != nullptr) {
     for (int t = 0; t < 4; ++t) {
       const fa_status st = check_strides(strides[t], B, H, N, d, dtype, t == 3);
@@ -114,7 +117,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   }
   if (dtype == FA_F32 && dropout_p > 0.0f) return FA_ERR_UNSUPPORTED;
   if (num_splits > 0) {
-    if (!is16(dtype)) return FA_ERR_UNSUPPORTED;
+    if (!mfma_path(dtype, d)) return FA_ERR_UNSUPPORTED;
     if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
     if (workspace_bytes < fa_fwd_split_workspace_size(B, H, N, d, dtype, num_splits))
       return FA_ERR_INVALID_ARG;
@@ -148,7 +151,13 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     a.opart = (float*)workspace;
     a.lsepart = (float*)((char*)workspace + pad256((size_t)num_splits * rows * d * 4));
   }
-  const hipError_t e = is16(dtype) ? fa::launch_fwd_16(a, stream) : fa::launch_fwd_f32(a, stream);
+  hipError_t e;
+  if (mfma_path(dtype, d))
+    e = fa::launch_fwd_16(a, stream);
+  else if (dtype == FA_F32 && (d == 64 || d == 128))
+    e = fa::launch_fwd_f32(a, stream);
+  else
+    e = fa::launch_fwd_generic(a, (int)dtype, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -183,7 +192,7 @@ fa_status fa_fwd_strided(const void* q, const void* k, const void* v, void* o, f
 }
 
 size_t fa_fwd_split_workspace_size(int B, int H, int N, int d, fa_dtype dtype, int num_splits) {
-  if (elems(B, H, N, d) < 0 || (d != 64 && d != 128) || !is16(dtype) || num_splits < 1 ||
+  if (elems(B, H, N, d) < 0 || !mfma_path(dtype, d) || num_splits < 1 ||
       num_splits > FA_MAX_SPLITS || !head_bytes_fit(N, d, dtype))
     return 0;
   const size_t rows = (size_t)B * H * N;
@@ -200,7 +209,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype) {
-  if (!is16(dtype) || (d != 64 && d != 128)) return 0;
+  if (!valid_dtype(dtype) || !fa::generic_head_size(d)) return 0;
   if (elems(B, H, N, d) < 0 || !head_bytes_fit(N, d, dtype)) return 0;
   return 2 * row_array_bytes(B, H, N);
 }
@@ -222,8 +231,8 @@ fa_status check_bwd(std::initializer_list<const void*> ptrs, const int32_t* key_
   if (!isfinite(scale) || scale <= 0.0f) return FA_ERR_INVALID_ARG;
   if (!valid_dropout(dropout_p)) return FA_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (!is16(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!fa::generic_head_size(d)) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32 && dropout_p > 0.0f) return FA_ERR_UNSUPPORTED;
   if (!head_bytes_fit(N, d, dtype)) return FA_ERR_UNSUPPORTED;
   if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d, dtype)) return FA_ERR_INVALID_ARG;
   return FA_OK;
@@ -262,7 +271,8 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.lse2 = (float*)((char*)workspace + row_array_bytes(B, H, N));
   fa::Strides* dst[8] = {&a.sq, &a.sk, &a.sv, &a.so, &a.sdo, &a.sdq, &a.sdk, &a.sdv};
   for (int t = 0; t < 8; ++t) *dst[t] = to_strides(strides ? &strides[t] : nullptr, H, N, d);
-  const hipError_t e = fa::launch_bwd_16(a, stages, stream);
+  const hipError_t e = mfma_path(dtype, d) ? fa::launch_bwd_16(a, stages, stream)
+                                           : fa::launch_bwd_generic(a, (int)dtype, stages, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -75,4 +75,11 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 enum : int { kBwdPre = 1, kBwdKV = 2, kBwdQ = 4, kBwdAll = kBwdQ | kBwdKV };
 hipError_t launch_bwd_16(const BwdArgs& a, int stages, hipStream_t s);  // bf16 or fp16
 
+// The generic (VALU, fp32-accumulating) kernels: element type `elem` (0 fp32,
+// 1 bf16, 2 fp16, the fa_dtype codes) and head size d with
+// generic_head_size(d); the same stage bits as launch_bwd_16.
+bool generic_head_size(int d);
+hipError_t launch_fwd_generic(const FwdArgs& a, int elem, hipStream_t s);
+hipError_t launch_bwd_generic(const BwdArgs& a, int elem, int stages, hipStream_t s);
+
 }  // namespace fa

@@ -75,8 +75,8 @@ def bwd(lib, ptrs=None, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, scale=0.12
     (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID),
     (dict(p=1.0), INVALID), (dict(p=-0.1), INVALID), (dict(p=float("nan")), INVALID),
     (dict(dtype=7), INVALID),
-    (dict(d=96), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
-    (dict(dtype=binding.FA_F32, p=0.1), UNSUPPORTED),
+    (dict(d=48), UNSUPPORTED), (dict(d=16), UNSUPPORTED), (dict(d=512), UNSUPPORTED),
+    (dict(d=0), INVALID), (dict(dtype=binding.FA_F32, p=0.1), UNSUPPORTED),
 ])
 def test_forward_rejects(lib, kw, expect):
     assert fwd(lib, **kw) == expect
@@ -84,7 +84,7 @@ def test_forward_rejects(lib, kw, expect):
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(B=0), INVALID), (dict(scale=float("nan")), INVALID), (dict(p=1.0), INVALID),
-    (dict(d=96), UNSUPPORTED), (dict(dtype=binding.FA_F32), UNSUPPORTED),
+    (dict(d=48), UNSUPPORTED), (dict(dtype=binding.FA_F32, p=0.1), UNSUPPORTED),
     (dict(ws=None), INVALID), (dict(ws=P + 4), INVALID), (dict(ws_bytes=0), INVALID),
 ])
 def test_backward_rejects(lib, kw, expect):
@@ -126,8 +126,10 @@ def test_workspace_size_is_linear_in_n():
     assert ws(4, 32, 4096, 128) == 2 * 4 * 32 * 4096 * 4
     assert ws(1, 8, 65536, 64) == 2 * 8 * 65536 * 4
     assert ws(1, 1, 65536, 64) < 65536 * 65536 // 16
-    assert ws(1, 1, 128, 96) == 0
-    assert ws(1, 1, 128, 64, binding.FA_F32) == 0
+    assert ws(1, 1, 128, 48) == 0
+    # the same two row arrays for every supported type and head size
+    for d in (32, 96, 256):
+        assert ws(3, 2, 100, d, binding.FA_F32) == ws(3, 2, 100, 64) == ws(3, 2, 100, d, binding.FA_F16)
     assert ws(0, 1, 128, 64) == 0
 
 
@@ -152,8 +154,8 @@ def stage_calls(lib, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, scale=0.125, 
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(B=0), INVALID), (dict(N=-3), INVALID), (dict(d=96), UNSUPPORTED),
-    (dict(dtype=binding.FA_F32), UNSUPPORTED), (dict(dtype=9), INVALID),
+    (dict(B=0), INVALID), (dict(N=-3), INVALID), (dict(d=48), UNSUPPORTED),
+    (dict(d=512), UNSUPPORTED), (dict(dtype=9), INVALID),
     (dict(ws=None), INVALID), (dict(ws=P + 4), INVALID), (dict(ws_bytes=0), INVALID),
 ])
 def test_backward_stages_reject(lib, kw, expect):
@@ -188,7 +190,7 @@ def test_split_workspace_size():
     # fp32 partial O per split (padded to 256 B) then fp32 partial LSE per split
     assert ws(2, 3, 100, 64, 4) == 4 * 2 * 3 * 100 * 64 * 4 + ((4 * 2 * 3 * 100 * 4 + 255) // 256) * 256
     assert ws(1, 8, 4096, 128, 1) == 8 * 4096 * 128 * 4 + 8 * 4096 * 4
-    assert ws(1, 1, 128, 96, 2) == 0
+    assert ws(1, 1, 128, 96, 2) == 0  # the split forward is for the MFMA head sizes only
     assert ws(1, 1, 128, 64, 0) == 0
     assert ws(1, 1, 128, 64, binding.FA_MAX_SPLITS + 1) == 0
     assert ws(1, 1, 128, 64, 2, binding.FA_F32) == 0
@@ -196,7 +198,8 @@ def test_split_workspace_size():
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(splits=0), INVALID), (dict(splits=binding.FA_MAX_SPLITS + 1), INVALID),
-    (dict(dtype=binding.FA_F32), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+    (dict(dtype=binding.FA_F32), UNSUPPORTED), (dict(d=96, ws_bytes=1 << 30), UNSUPPORTED),
+    (dict(d=256, ws_bytes=1 << 30), UNSUPPORTED),
     (dict(ws=None), INVALID), (dict(ws=P + 8), INVALID), (dict(ws_bytes=16), INVALID),
     (dict(q=None), INVALID), (dict(p=1.0), INVALID), (dict(N=0), INVALID),
 ])
@@ -211,7 +214,7 @@ def noalloc(lib, ptrs=None, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, scale=
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(B=0), INVALID), (dict(scale=float("nan")), INVALID), (dict(p=1.0), INVALID),
-    (dict(d=96), UNSUPPORTED), (dict(dtype=binding.FA_F32), UNSUPPORTED),
+    (dict(d=48), UNSUPPORTED), (dict(dtype=binding.FA_F32, p=0.1), UNSUPPORTED),
     (dict(N=1 << 24, d=128), UNSUPPORTED),
     # one query row past the fixed scratch (2 x 4 bytes per row): refused on the
     # host before any HIP call
@@ -241,8 +244,7 @@ def test_noalloc_limit_is_the_workspace_of_4m_rows(lib):
 #
 # No call here may pass every check: it would launch kernels on the dummy
 # pointers.  Strides that are accepted are shown with a later check failing
-# instead (fp32 with dropout in the forward, fp32 in the backward: both are
-# UNSUPPORTED only once the strides have passed).
+# instead (fp32 with dropout, UNSUPPORTED only once the strides have passed).
 
 
 def contig(H, N, d):
@@ -266,15 +268,15 @@ def fwd_s_accepts(lib, rows, **kw):
     return fwd_s(lib, rows, dtype=binding.FA_F32, p=0.1, **kw) == UNSUPPORTED
 
 
-def bwd_s(lib, rows, B=2, H=2, N=128, d=64, dtype=binding.FA_BF16):
+def bwd_s(lib, rows, B=2, H=2, N=128, d=64, dtype=binding.FA_BF16, p=0.0):
     ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d, binding.FA_BF16)
-    return lib.fa_bwd_strided(*([P] * 9), strides_arr(rows), B, H, N, d, dtype, 0.125, 0, None, 0.0,
+    return lib.fa_bwd_strided(*([P] * 9), strides_arr(rows), B, H, N, d, dtype, 0.125, 0, None, p,
                               0, P, ws_bytes, None)
 
 
 def bwd_s_accepts(lib, rows):
-    """The strides pass (the fp32 backward is then the first check to fail)."""
-    return bwd_s(lib, rows, dtype=binding.FA_F32) == UNSUPPORTED
+    """The strides pass (fp32 with dropout is then the first check to fail)."""
+    return bwd_s(lib, rows, dtype=binding.FA_F32, p=0.1) == UNSUPPORTED
 
 
 @pytest.mark.parametrize("which", range(4))
@@ -326,14 +328,14 @@ def test_strided_backward_outputs_must_not_overlap(lib):
 
 def test_fp16_is_a_16_bit_type_everywhere(lib):
     f16 = binding.FA_F16
-    assert fwd(lib, dtype=f16, d=96) == UNSUPPORTED   # recognised, d still checked
+    assert fwd(lib, dtype=f16, d=48) == UNSUPPORTED   # recognised, d still checked
     assert fwd(lib, dtype=f16, p=1.0) == INVALID
     assert fwd(lib, dtype=3) == INVALID
     assert lib.fa_bwd_workspace_size(1, 1, 128, 64, f16) == \
         lib.fa_bwd_workspace_size(1, 1, 128, 64, binding.FA_BF16)
     assert lib.fa_fwd_split_workspace_size(1, 1, 128, 64, f16, 2) == \
         lib.fa_fwd_split_workspace_size(1, 1, 128, 64, binding.FA_BF16, 2)
-    assert bwd(lib, dtype=f16, d=96) == UNSUPPORTED
+    assert bwd(lib, dtype=f16, d=48) == UNSUPPORTED
     # fp16 rows of 16 bytes: strides in units of 8 elements, like bf16
     rows = [contig(2, 128, 64)] * 4
     rows[0] = (2 * 128 * 64, 128 * 64, 68)

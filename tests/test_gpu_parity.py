@@ -237,6 +237,30 @@ def test_workload_padded_dropout():
         check_bwd([t[sl] for t in g], [r[sl] for r in ref], what=f"padded_dropout head {(b, h)}")
 
 
+def test_workload_causal_padded_dropout():
+    # The padded-dropout workload's inputs (B=16, H=12, N=2048, d=64, key
+    # lengths U{512..2048}, p = 0.1) with the causal mask as well: both masks
+    # and dropout at once, at full size.  Oracle on three whole heads.
+    w = WORKLOADS[4]
+    inp = draw_workload(w)
+    seed = 0x0123456789ABCDEF
+    kl = key_lens_list(inp)
+    note(f"causal_padded_dropout B16 H12 N2048 d64 p=0.1 key_lens={kl}")
+    o, lse = gpu_forward(inp, w.scale, True, w.dropout_p, seed)
+    g = gpu_backward(inp, o, lse, w.scale, True, w.dropout_p, seed)
+    heads = [(int(np.argmin(kl)), 3), (int(np.argmax(kl)), 8), (9, 0)]
+    ro, rlse = attention_forward(inp.q, inp.k, inp.v, w.scale, True, kl, w.dropout_p, seed,
+                                 heads=heads)
+    ref = attention_backward(inp.q, inp.k, inp.v, inp.dout, w.scale, True, kl, w.dropout_p,
+                             seed, heads=heads)
+    for b, h in heads:
+        sl = slice(b, b + 1), slice(h, h + 1)
+        check_fwd(o[sl], lse[sl], ro[sl], rlse[sl],
+                  what=f"causal_padded_dropout head {(b, h)} L={kl[b]}")
+        check_bwd([t[sl] for t in g], [r[sl] for r in ref],
+                  what=f"causal_padded_dropout head {(b, h)}")
+
+
 def test_workload_long_causal():
     # N = 65536: O, LSE and dQ on 64 sampled query rows of all 8 heads; dK and dV
     # on sampled keys of the last 4096 positions of two heads (causal: only the
