@@ -39,18 +39,38 @@ def _from_bhnd(t, layout):
     return t if layout == "bhnd" else t.transpose(1, 2)
 
 
+def split_count(B, H, N, d, causal, cus):
+    """Key splits for the forward of one shape (0: the plain fa_fwd).
+
+    The plain forward launches one workgroup per 128-query block (causal ones
+    in pairs, so each has the same work).  When that leaves CUs idle, the
+    split forward (one workgroup per query block and key share) gets enough
+    shares for one workgroup per CU, at least 2, capped so that every share
+    keeps at least four 64-key tiles of the longest block and at
+    FA_MAX_SPLITS.  (Measured on small shapes: more shares than that lose
+    more to the combine pass and the shorter shares than they gain.)  Only
+    the MFMA head sizes have a split forward.
+    """
+    if d not in (64, 128):
+        return 0
+    blocks = (N + 127) // 128
+    plain = B * H * ((blocks + 1) // 2 if causal else blocks)
+    if plain >= cus:
+        return 0
+    want = max(2, -(-cus // (B * H * blocks)))  # ceil
+    cap = min(max(((N + 63) // 64) // 4, 1), binding.FA_MAX_SPLITS)
+    s = min(want, cap)
+    return s if s >= 2 else 0
+
+
 def _splits(q, causal):
-    """Key splits for the forward: 2 (fa_fwd_split) when the plain forward
-    would launch fewer workgroups than the GPU has CUs (one per 128-query block,
-    causal ones in pairs), else 0 (fa_fwd).  16-bit types on a GPU, contiguous
-    tensors only (the split entry point takes no strides)."""
+    """split_count for q's shape on its GPU: 16-bit types, contiguous tensors
+    only (the split entry point takes no strides)."""
     if q.dtype not in (torch.bfloat16, torch.float16) or not q.is_cuda or not q.is_contiguous():
         return 0
-    B, H, N, _ = q.shape
-    blocks = (N + 127) // 128
-    workgroups = B * H * ((blocks + 1) // 2 if causal else blocks)
+    B, H, N, d = q.shape
     cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-    return 2 if workgroups < cus else 0
+    return split_count(B, H, N, d, causal, cus)
 
 
 def _forward(q, k, v, scale, causal, key_lens, dropout_p, seed):

@@ -39,3 +39,22 @@ def test_layout_views_are_passed_without_copies():
     assert autograd._to_bhnd(e, "bhnd").is_contiguous()
     odd = torch.zeros(2, 4, 100, 72, dtype=torch.bfloat16)[..., 4:68]  # rows start 8 bytes in
     assert not binding.kernel_layout_ok(odd)
+
+
+def test_split_count_per_shape():
+    from io_aware_exact_24_amd.autograd import split_count
+
+    cus = 256
+    # shapes that fill the GPU with the plain forward take no split
+    assert split_count(4, 32, 4096, 128, True, cus) == 0
+    assert split_count(8, 16, 1024, 64, False, cus) == 0
+    # few query blocks: enough shares for one workgroup per CU, at least 2 ...
+    assert split_count(1, 1, 4096, 128, True, cus) == 8    # 32 blocks x 8 = 256
+    assert split_count(1, 8, 2048, 64, False, cus) == 2    # 128 blocks x 2 = 256
+    assert split_count(1, 4, 8192, 128, True, cus) == 2    # 128 causal pairs: at least 2
+    # ... but at least four 64-key tiles per share, and at most FA_MAX_SPLITS
+    assert split_count(1, 2, 1000, 128, True, cus) == 4    # 16 tiles -> 4 shares
+    assert split_count(1, 1, 128, 64, False, cus) == 0     # 2 tiles: nothing to split
+    assert split_count(1, 1, 1 << 16, 128, False, 1 << 15) == 64
+    # only the MFMA head sizes have a split forward
+    assert split_count(1, 1, 4096, 96, True, cus) == 0
