@@ -34,9 +34,10 @@
  * contiguous, element type `dtype`; contiguous ([B, H, N, d] row-major) for
  * every entry point except fa_fwd_strided and fa_bwd_strided, which take
  * each tensor's batch, head and row strides (fa_strides), so that, e.g.,
- * [B, N, H, d] memory or a fused QKV projection is read in place.  LSE:
+ * [B, N, H, d] memory or a fused QKV projection is read in place, and the
+ * packed-sequence entry points (fa_fwd_varlen, fa_bwd_varlen).  LSE:
  * contiguous fp32 [B, H, N].  key_lens: device int32 [B] or NULL.  All
- * pointers are device pointers, 16-byte aligned.
+ * pointers are device pointers, 16-byte aligned (LSE: 4-byte aligned).
  *
  * Ownership.  The caller allocates and owns every buffer, including the
  * backward workspace.  The library never allocates or frees device memory,
@@ -173,6 +174,45 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
                        const int32_t* key_lens, float dropout_p, uint64_t seed, int num_splits,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Packed batches of sequences of different lengths, without padding.
+ * Sequence b (0 <= b < num_seqs) is the token rows [cu_seqlens[b],
+ * cu_seqlens[b + 1]) of every tensor; the tensors are [T, H, d] with
+ * T = cu_seqlens[num_seqs] tokens, rows of d contiguous elements.
+ *   strides     strides[t].row and strides[t].head are tensor t's token and
+ *               head strides in elements (q, k, v, o here; q, k, v, o, dout,
+ *               dq, dk, dv in fa_bwd_varlen); `batch` is ignored.  NULL:
+ *               every tensor contiguous [T, H, d] (row = H * d, head = d).
+ *               The fa_strides rules apply with B = 1 and N = T (outputs
+ *               one-to-one over all tokens) and with N = the longest
+ *               sequence (the 32-bit span).
+ *   cu_seqlens  HOST int32 array of num_seqs + 1 offsets, cu_seqlens[0] = 0,
+ *               non-decreasing (empty sequences allowed); read during the
+ *               call only.
+ *   lse         fp32; sequence b's LSE is the contiguous [H, len_b] block at
+ *               lse + H * cu_seqlens[b].
+ * Each sequence attends to its own tokens only (causal: key j <= query i,
+ * positions inside the sequence); the dropout counter of fa.h uses b as the
+ * batch index and positions inside the sequence as i and j.  Everything else
+ * (dtype, d, scale, dropout, checks, kernels) is fa_fwd's / fa_bwd's; the
+ * kernels run once per non-empty sequence, in order, on `stream`.
+ * fa_bwd_varlen's workspace: fa_bwd_varlen_workspace_size() bytes (the
+ * per-row terms of the longest sequence; the sequences reuse it in stream
+ * order).
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const fa_strides* strides, const int32_t* cu_seqlens, int num_seqs,
+                        int H, int d, fa_dtype dtype, float scale, int causal, float dropout_p,
+                        uint64_t seed, hipStream_t stream);
+size_t fa_bwd_varlen_workspace_size(const int32_t* cu_seqlens, int num_seqs, int H, int d,
+                                    fa_dtype dtype);
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        const fa_strides* strides, const int32_t* cu_seqlens, int num_seqs,
+                        int H, int d, fa_dtype dtype, float scale, int causal, float dropout_p,
+                        uint64_t seed, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: two fp32 [B, H, N]

@@ -18,7 +18,8 @@ FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_split", "fa_fwd_split_workspace_size",
-           "fa_bwd_noalloc", "fa_fwd_strided", "fa_bwd_strided")
+           "fa_bwd_noalloc", "fa_fwd_strided", "fa_bwd_strided", "fa_fwd_varlen", "fa_bwd_varlen",
+           "fa_bwd_varlen_workspace_size")
 FA_MAX_SPLITS = 64
 FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -76,6 +77,14 @@ def load_library():
     sp = ctypes.POINTER(FaStrides)
     lib.fa_fwd_strided.restype = i
     lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, sp, i, i, i, i, i, f, i, vp, f, u64, vp]
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.fa_fwd_varlen.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, sp, ip, i, i, i, i, f, i, f, u64, vp]
+    lib.fa_bwd_varlen_workspace_size.restype = sz
+    lib.fa_bwd_varlen_workspace_size.argtypes = [ip, i, i, i, i]
+    lib.fa_bwd_varlen.restype = i
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sp, ip, i, i, i, i, f, i, f, u64,
+                                  vp, sz, vp]
     lib.fa_bwd_strided.restype = i
     lib.fa_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sp, i, i, i, i, i, f, i, vp,
                                    f, u64, vp, sz, vp]
@@ -284,6 +293,105 @@ def fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_l
                             _ptr(workspace), ws_bytes, _stream(stream, q.device))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_strided")
+
+
+def _cu(cu_seqlens):
+    """Host int32 array of the sequence offsets (a list, numpy array or CPU tensor)."""
+    vals = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    return (ctypes.c_int32 * len(vals))(*vals), len(vals) - 1
+
+
+def _packed_strides(tensors):
+    arr = (FaStrides * len(tensors))()
+    for a, t in zip(arr, tensors):
+        a.batch, a.head, a.row = 0, t.stride(1), t.stride(0)
+    return arr
+
+
+def _check_packed(t, shape, dtype, device, name):
+    if t.shape != shape or t.dtype != dtype or t.device != device or t.stride(-1) != 1:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype} on {device} with a contiguous "
+                         f"last dimension, got {tuple(t.shape)} {t.dtype} on {t.device} strides "
+                         f"{t.stride()}")
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, scale, causal=False, dropout_p=0.0, seed=0,
+                  stream=None):
+    """fa_fwd_varlen: packed [T, H, d] tensors (any token and head strides),
+    sequence b = tokens [cu_seqlens[b], cu_seqlens[b+1]) (host offsets); lse:
+    fp32 with H * T elements (sequence b's [H, len] block at H * cu_seqlens[b])."""
+    import torch
+
+    lib = load_library()
+    T, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_packed(t, q.shape, q.dtype, q.device, name)
+    if lse.dtype != torch.float32 or lse.numel() != H * T or not lse.is_contiguous():
+        raise ValueError("lse: expected a contiguous fp32 tensor of H * T elements")
+    cu, n = _cu(cu_seqlens)
+    if n < 1 or cu[n] != T:
+        raise ValueError(f"cu_seqlens must end at T = {T}")
+    st = lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                           _packed_strides((q, k, v, o)), cu, n, H, d, _dtype_code(q), float(scale),
+                           int(bool(causal)), float(dropout_p), int(seed), _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_varlen")
+
+
+def fa_bwd_varlen_workspace_size(cu_seqlens, H, d, dtype_code=FA_BF16):
+    cu, n = _cu(cu_seqlens)
+    return int(load_library().fa_bwd_varlen_workspace_size(cu, n, H, d, dtype_code))
+
+
+def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, scale, causal=False, dropout_p=0.0,
+                  seed=0, workspace=None, stream=None):
+    """fa_bwd_varlen on packed [T, H, d] tensors (see fa_fwd_varlen)."""
+    import torch
+
+    lib = load_library()
+    T, H, d = q.shape
+    ts = (q, k, v, o, dout, dq, dk, dv)
+    for name, t in zip(("q", "k", "v", "o", "dout", "dq", "dk", "dv"), ts):
+        _check_packed(t, q.shape, q.dtype, q.device, name)
+    if lse.dtype != torch.float32 or lse.numel() != H * T or not lse.is_contiguous():
+        raise ValueError("lse: expected a contiguous fp32 tensor of H * T elements")
+    cu, n = _cu(cu_seqlens)
+    if n < 1 or cu[n] != T:
+        raise ValueError(f"cu_seqlens must end at T = {T}")
+    if workspace is None:
+        raise ValueError("fa_bwd_varlen needs a workspace tensor (see fa_bwd_varlen_workspace_size)")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _packed_strides(ts), cu, n, H, d, _dtype_code(q),
+                           float(scale), int(bool(causal)), float(dropout_p), int(seed),
+                           _ptr(workspace), ws_bytes, _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_varlen")
+
+
+def forward_varlen(q, k, v, cu_seqlens, scale, causal=False, dropout_p=0.0, seed=0, stream=None):
+    """Allocate O (in q's layout) and LSE and call fa_fwd_varlen."""
+    import torch
+
+    T, H, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(H * T, dtype=torch.float32, device=q.device)
+    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, scale, causal, dropout_p, seed, stream)
+    return o, lse
+
+
+def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, scale, causal=False, dropout_p=0.0, seed=0,
+                    stream=None):
+    """Allocate dQ, dK, dV and the workspace and call fa_bwd_varlen."""
+    import torch
+
+    T, H, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = fa_bwd_varlen_workspace_size(cu_seqlens, H, d, _dtype_code(q))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, scale, causal, dropout_p, seed, ws,
+                  stream)
+    return dq, dk, dv
 
 
 def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None,

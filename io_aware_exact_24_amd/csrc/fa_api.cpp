@@ -14,6 +14,7 @@
 namespace {
 
 bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
 
 // Element count of one [B, H, N, d] tensor, or -1 when it would overflow int64
 // or the per-kernel 32-bit index ranges (rows B*H*N must fit in int32).
@@ -42,8 +43,11 @@ bool head_bytes_fit(int N, int64_t row_stride, fa_dtype dtype) {
 }
 
 // The fa_strides rules of fa.h for one tensor (`output`: it is written).
+// The rows are one-to-one over B x H x N (n_map, below) and one slice spans
+// n_span rows (n_span = N except for packed sequences, where it is the
+// longest sequence).
 fa_status check_strides(const fa_strides& s, int B, int H, int N, int d, fa_dtype dtype,
-                        bool output) {
+                        bool output, int n_span = -1) {
   const int64_t unit = 16 / (int64_t)elem_bytes(dtype);  // elements per 16 bytes
   if (s.batch < 0 || s.head < 0 || s.row < d) return FA_ERR_INVALID_ARG;
   if (s.batch % unit != 0 || s.head % unit != 0 || s.row % unit != 0) return FA_ERR_INVALID_ARG;
@@ -67,7 +71,7 @@ fa_status check_strides(const fa_strides& s, int B, int H, int N, int d, fa_dtyp
       span = dm.stride * (dm.extent - 1) + span;
     }
   }
-  if (!head_bytes_fit(N, s.row, dtype)) return FA_ERR_UNSUPPORTED;
+  if (!head_bytes_fit(n_span < 0 ? N : n_span, s.row, dtype)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -98,8 +102,9 @@ size_t pad256(size_t n) { return (n + 255) & ~(size_t)255; }
 fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                   const fa_strides* strides, int B, int H, int N, int d, fa_dtype dtype,
                   float scale, int causal, const int32_t* key_lens, float dropout_p, uint64_t seed,
-                  int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+                  int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                  int b0 = 0) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
     return FA_ERR_INVALID_ARG;
   if (key_lens != nullptr && ((uintptr_t)key_lens & 3u) != 0) return FA_ERR_INVALID_ARG;
   if (elems(B, H, N, d) < 0) return FA_ERR_INVALID_ARG;
@@ -145,6 +150,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   a.drop_threshold = drop_threshold(dropout_p);
   a.drop_scale = drop_scale(dropout_p);
   a.seed = seed;
+  a.b0 = b0;
   if (num_splits > 0) {
     const size_t rows = (size_t)B * H * N;
     a.num_splits = num_splits;
@@ -220,11 +226,17 @@ namespace {
 
 // Checks shared by fa_bwd and its stages; pointers that a stage does not use
 // are passed as a non-null aligned placeholder by that stage.
-fa_status check_bwd(std::initializer_list<const void*> ptrs, const int32_t* key_lens, int B, int H,
-                    int N, int d, fa_dtype dtype, float scale, float dropout_p,
-                    const void* workspace, size_t workspace_bytes) {
+// Stands for a tensor a stage does not read: aligned, never dereferenced.
+const void* const kUnused = (const void*)(uintptr_t)16;
+const float* const kNoLse = (const float*)kUnused;
+
+// `lse` (when the stage reads it) needs 4-byte alignment only.
+fa_status check_bwd(std::initializer_list<const void*> ptrs, const float* lse, int B, int H, int N,
+                    int d, fa_dtype dtype, float scale, float dropout_p, const void* workspace,
+                    size_t workspace_bytes, const int32_t* key_lens = nullptr) {
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return FA_ERR_INVALID_ARG;
+  if (lse != kNoLse && !aligned4(lse)) return FA_ERR_INVALID_ARG;
   if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
   if (key_lens != nullptr && ((uintptr_t)key_lens & 3u) != 0) return FA_ERR_INVALID_ARG;
   if (elems(B, H, N, d) < 0) return FA_ERR_INVALID_ARG;
@@ -243,7 +255,7 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, const fa_strides* strides, int B,
                   int H, int N, int d, fa_dtype dtype, float scale, int causal,
                   const int32_t* key_lens, float dropout_p, uint64_t seed, void* workspace,
-                  int stages, hipStream_t stream) {
+                  int stages, hipStream_t stream, int b0 = 0) {
   fa::BwdArgs a;
   a.fp16 = dtype == FA_F16;
   a.q = q;
@@ -266,6 +278,7 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.drop_threshold = drop_threshold(dropout_p);
   a.drop_scale = drop_scale(dropout_p);
   a.seed = seed;
+  a.b0 = b0;
   // workspace: D, then LSE * log2(e)
   a.delta = (float*)workspace;
   a.lse2 = (float*)((char*)workspace + row_array_bytes(B, H, N));
@@ -276,7 +289,6 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-const void* const kUnused = (const void*)(uintptr_t)16;  // aligned, never dereferenced
 
 }  // namespace
 
@@ -286,8 +298,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                  fa_dtype dtype, float scale, int causal, const int32_t* key_lens, float dropout_p,
                  uint64_t seed, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const fa_status st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, key_lens, B, H, N, d, dtype,
-                                 scale, dropout_p, workspace, workspace_bytes);
+  const fa_status st = check_bwd({q, k, v, o, dout, dq, dk, dv}, lse,
+                                 B, H, N, d, dtype, scale, dropout_p, workspace, workspace_bytes,
+                                 key_lens);
   if (st != FA_OK) return st;
   return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, nullptr, B, H, N, d, dtype, scale, causal,
                  key_lens, dropout_p, seed, workspace, fa::kBwdAll, stream);
@@ -307,8 +320,9 @@ fa_status fa_bwd_strided(const void* q, const void* k, const void* v, const void
       if (st != FA_OK) return st;
     }
   }
-  const fa_status st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, key_lens, B, H, N, d, dtype,
-                                 scale, dropout_p, workspace, workspace_bytes);
+  const fa_status st = check_bwd({q, k, v, o, dout, dq, dk, dv}, lse,
+                                 B, H, N, d, dtype, scale, dropout_p, workspace, workspace_bytes,
+                                 key_lens);
   if (st != FA_OK) return st;
   return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, strides, B, H, N, d, dtype, scale, causal,
                  key_lens, dropout_p, seed, workspace, fa::kBwdAll, stream);
@@ -317,34 +331,149 @@ fa_status fa_bwd_strided(const void* q, const void* k, const void* v, const void
 fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N,
                             int d, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-  const fa_status st = check_bwd({o, dout, lse}, nullptr, B, H, N, d, dtype, 1.0f, 0.0f, workspace,
-                                 workspace_bytes);
+  const fa_status st = check_bwd({o, dout}, lse,
+                                 B, H, N, d, dtype, 1.0f, 0.0f, workspace, workspace_bytes);
   if (st != FA_OK) return st;
-  return run_bwd(kUnused, kUnused, kUnused, o, dout, lse, nullptr, nullptr, nullptr, nullptr, B, H, N,
-                 d, dtype, 1.0f, 0, nullptr, 0.0f, 0, workspace, fa::kBwdPre, stream);
+  return run_bwd(kUnused, kUnused, kUnused, o, dout, lse, nullptr, nullptr, nullptr, nullptr, B, H,
+                 N, d, dtype, 1.0f, 0, nullptr, 0.0f, 0, workspace, fa::kBwdPre, stream);
 }
 
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
                       void* dv, int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
                       const int32_t* key_lens, float dropout_p, uint64_t seed,
                       const void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const fa_status st = check_bwd({q, k, v, dout, dk, dv}, key_lens, B, H, N, d, dtype, scale,
-                                 dropout_p, workspace, workspace_bytes);
+  const fa_status st = check_bwd({q, k, v, dout, dk, dv}, kNoLse,
+                                 B, H, N, d, dtype, scale, dropout_p, workspace, workspace_bytes,
+                                 key_lens);
   if (st != FA_OK) return st;
-  return run_bwd(q, k, v, kUnused, dout, (const float*)kUnused, nullptr, dk, dv, nullptr, B, H, N, d,
-                 dtype, scale, causal, key_lens, dropout_p, seed, (void*)workspace, fa::kBwdKV,
-                 stream);
+  return run_bwd(q, k, v, kUnused, dout, kNoLse, nullptr, dk, dv, nullptr, B, H, N, d, dtype, scale,
+                 causal, key_lens, dropout_p, seed, (void*)workspace, fa::kBwdKV, stream);
 }
 
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, int B, int H, int N, int d, fa_dtype dtype,
                     float scale, int causal, const int32_t* key_lens, float dropout_p,
                     uint64_t seed, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const fa_status st = check_bwd({q, k, v, o, dout, lse, dq}, key_lens, B, H, N, d, dtype, scale,
-                                 dropout_p, workspace, workspace_bytes);
+  const fa_status st = check_bwd({q, k, v, o, dout, dq}, lse,
+                                 B, H, N, d, dtype, scale, dropout_p, workspace, workspace_bytes,
+                                 key_lens);
   if (st != FA_OK) return st;
   return run_bwd(q, k, v, o, dout, lse, dq, nullptr, nullptr, nullptr, B, H, N, d, dtype, scale,
                  causal, key_lens, dropout_p, seed, workspace, fa::kBwdQ, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Packed sequences: the kernels once per sequence, on offset pointers.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// cu_seqlens: starts at 0, non-decreasing.  Longest sequence and total tokens.
+fa_status check_seqs(const int32_t* cu, int num_seqs, int* longest, int* total) {
+  if (cu == nullptr || num_seqs < 1 || cu[0] != 0) return FA_ERR_INVALID_ARG;
+  int mx = 0;
+  for (int b = 0; b < num_seqs; ++b) {
+    if (cu[b + 1] < cu[b]) return FA_ERR_INVALID_ARG;
+    mx = std::max(mx, cu[b + 1] - cu[b]);
+  }
+  *longest = mx;
+  *total = cu[num_seqs];
+  return FA_OK;
+}
+
+// Per-sequence strides of n tensors (the first `first_output` are read,
+// the rest written), checked over the whole packed tensors: rows one-to-one
+// over all `total` tokens, a slice of `longest` rows within 32 bits.
+fa_status packed_strides(const fa_strides* in, int n, int first_output, int H, int total,
+                         int longest, int d, fa_dtype dtype, fa_strides* out) {
+  for (int t = 0; t < n; ++t) {
+    out[t] = in ? fa_strides{0, in[t].head, in[t].row} : fa_strides{0, d, (int64_t)H * d};
+    const fa_status st =
+        check_strides(out[t], 1, H, std::max(total, 1), d, dtype, t >= first_output, longest);
+    if (st != FA_OK) return st;
+  }
+  return FA_OK;
+}
+
+template <typename P>
+P at_row(P base, int64_t row, const fa_strides& s, fa_dtype dtype) {
+  return (P)((const char*)base + row * s.row * (int64_t)elem_bytes(dtype));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const fa_strides* strides, const int32_t* cu_seqlens, int num_seqs,
+                        int H, int d, fa_dtype dtype, float scale, int causal, float dropout_p,
+                        uint64_t seed, hipStream_t stream) {
+  int longest = 0, total = 0;
+  fa_status st = check_seqs(cu_seqlens, num_seqs, &longest, &total);
+  if (st != FA_OK) return st;
+  if (H <= 0 || d <= 0 || !valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
+  if (!fa::generic_head_size(d)) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  fa_strides s[4];
+  st = packed_strides(strides, 4, 3, H, total, longest, d, dtype, s);
+  if (st != FA_OK) return st;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t t0 = cu_seqlens[b];
+    const int len = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (len == 0) continue;
+    st = run_fwd(at_row(q, t0, s[0], dtype), at_row(k, t0, s[1], dtype), at_row(v, t0, s[2], dtype),
+                 at_row(o, t0, s[3], dtype), lse + (int64_t)H * t0, s, 1, H, len, d, dtype, scale,
+                 causal, nullptr, dropout_p, seed, 0, nullptr, 0, stream, b);
+    if (st != FA_OK) return st;
+  }
+  return FA_OK;
+}
+
+size_t fa_bwd_varlen_workspace_size(const int32_t* cu_seqlens, int num_seqs, int H, int d,
+                                    fa_dtype dtype) {
+  int longest = 0, total = 0;
+  if (check_seqs(cu_seqlens, num_seqs, &longest, &total) != FA_OK || longest == 0) return 0;
+  return fa_bwd_workspace_size(1, H, longest, d, dtype);
+}
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        const fa_strides* strides, const int32_t* cu_seqlens, int num_seqs,
+                        int H, int d, fa_dtype dtype, float scale, int causal, float dropout_p,
+                        uint64_t seed, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  int longest = 0, total = 0;
+  fa_status st = check_seqs(cu_seqlens, num_seqs, &longest, &total);
+  if (st != FA_OK) return st;
+  if (H <= 0 || d <= 0 || !valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
+  if (!fa::generic_head_size(d)) return FA_ERR_UNSUPPORTED;
+  fa_strides s[8];
+  st = packed_strides(strides, 8, 5, H, total, longest, d, dtype, s);
+  if (st != FA_OK) return st;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t t0 = cu_seqlens[b];
+    const int len = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (len == 0) continue;
+    const void* qb = at_row(q, t0, s[0], dtype);
+    const void* kb = at_row(k, t0, s[1], dtype);
+    const void* vb = at_row(v, t0, s[2], dtype);
+    const void* ob = at_row(o, t0, s[3], dtype);
+    const void* dob = at_row(dout, t0, s[4], dtype);
+    void* dqb = at_row(dq, t0, s[5], dtype);
+    void* dkb = at_row(dk, t0, s[6], dtype);
+    void* dvb = at_row(dv, t0, s[7], dtype);
+    const float* lb = lse + (int64_t)H * t0;
+    st = check_bwd({qb, kb, vb, ob, dob, dqb, dkb, dvb}, lb, 1, H, len, d, dtype, scale, dropout_p,
+                   workspace, workspace_bytes);
+    if (st != FA_OK) return st;
+    st = run_bwd(qb, kb, vb, ob, dob, lb, dqb, dkb, dvb, s, 1, H, len, d, dtype, scale, causal,
+                 nullptr, dropout_p, seed, workspace, fa::kBwdAll, stream, b);
+    if (st != FA_OK) return st;
+  }
+  return FA_OK;
 }
 
 }  // extern "C"
@@ -408,8 +537,8 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void
   // workspace (a placeholder address here: nothing is launched before the
   // real one is known), then the size limit, all before any HIP call.
   const size_t need = fa_bwd_workspace_size(B, H, N, d, dtype);
-  fa_status st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, key_lens, B, H, N, d, dtype, scale,
-                           dropout_p, kUnused, need);
+  fa_status st = check_bwd({q, k, v, o, dout, dq, dk, dv}, lse,
+                           B, H, N, d, dtype, scale, dropout_p, kUnused, need, key_lens);
   if (st != FA_OK) return st;
   if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
   void* ws = nullptr;

@@ -29,6 +29,7 @@ hipError_t launch_bwd_16(const BwdArgs& a, int stages, hipStream_t s) {
   p.key_lens = a.key_lens;
   p.H = a.H;
   p.N = a.N;
+  p.b0 = a.b0;
   p.num_blocks = 0;
   p.units = 0;
   p.scale = a.scale;

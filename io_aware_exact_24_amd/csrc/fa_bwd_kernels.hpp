@@ -65,6 +65,7 @@ struct BwdParams {
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   const int32_t* key_lens;
   int H, N, num_blocks;
+  int b0;  // added to the batch index in the dropout counter
   int units;  // dK/dV work units (blocks, or causal pairs of blocks) over all heads
   float scale, scale_log2;
   uint32_t drop_threshold;
@@ -89,7 +90,7 @@ using P1 = std::integral_constant<int, 1>;
 
 // Dropout keep factor of element (row, key): 1/(1-p) or 0.
 __device__ __forceinline__ float dropout_z(const BwdParams& p, int row, int key, int hi, int bi) {
-  const u32x4 w = philox((uint32_t)key >> 2, (uint32_t)row, (uint32_t)hi, (uint32_t)bi, p.seed_lo,
+  const u32x4 w = philox((uint32_t)key >> 2, (uint32_t)row, (uint32_t)hi, (uint32_t)(bi + p.b0), p.seed_lo,
                          p.seed_hi);
   const uint32_t word = philox_word(w, key);
   return word >= p.drop_threshold ? p.drop_scale : 0.0f;
@@ -122,7 +123,7 @@ using Stage = std::integral_constant<int, S % 3>;
 __device__ __forceinline__ uint32_t quad_keep4(const BwdParams& p, int row0, int key, int hi,
                                                int bi) {
   const int q = threadIdx.x & 3;
-  const u32x4 w = philox((uint32_t)key >> 2, (uint32_t)(row0 + q), (uint32_t)hi, (uint32_t)bi,
+  const u32x4 w = philox((uint32_t)key >> 2, (uint32_t)(row0 + q), (uint32_t)hi, (uint32_t)(bi + p.b0),
                          p.seed_lo, p.seed_hi);
   uint32_t bits = 0;
   static_for<4>([&](auto j_t) {

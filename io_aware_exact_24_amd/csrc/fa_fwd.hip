@@ -46,6 +46,7 @@ struct FwdParams {
   const int32_t* key_lens;
   Strides sq, sk, sv, so;  // element strides (batch, head, row); d is contiguous
   int H, N, num_qblocks;
+  int b0;  // added to the batch index in the dropout counter
   int causal;  // fp32 kernel only (the 16-bit kernel takes it as a template argument)
   float scale_log2;  // scale * log2(e): scores enter exp2 in these units
   uint32_t drop_threshold;
@@ -381,7 +382,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const uint32_t key4 = (uint32_t)((jt0 + j) * BN + 32 * t + 8 * g + 4 * hh);
-          const u32x4 w = philox(key4 >> 2, (uint32_t)qi, (uint32_t)hi, (uint32_t)bi, p.seed_lo,
+          const u32x4 w = philox(key4 >> 2, (uint32_t)qi, (uint32_t)hi, (uint32_t)(bi + p.b0), p.seed_lo,
                                  p.seed_hi);
 #pragma unroll
           for (int x = 0; x < 4; ++x)
@@ -671,6 +672,7 @@ FwdParams make_params(const FwdArgs& a) {
   p.so = a.so;
   p.H = a.H;
   p.N = a.N;
+  p.b0 = a.b0;
   p.num_qblocks = 0;
   p.causal = a.causal != 0;
   p.scale_log2 = a.scale * kLog2e;

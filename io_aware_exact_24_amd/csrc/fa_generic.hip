@@ -50,6 +50,7 @@ struct GParams {
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   const int32_t* key_lens;
   int H, N;
+  int b0;  // added to the batch index in the dropout counter
   float scale;
   int causal;
   int dropout;
@@ -102,7 +103,8 @@ __device__ __forceinline__ float row_sum(float x) {
 
 // Dropout factor of element (query i, key j) of head (b, h): 1/(1-p) or 0.
 __device__ __forceinline__ float keep_factor(const GParams& p, int i, int j, int hi, int bi) {
-  const u32x4 w = philox((uint32_t)j >> 2, (uint32_t)i, (uint32_t)hi, (uint32_t)bi, p.seed_lo, p.seed_hi);
+  const u32x4 w = philox((uint32_t)j >> 2, (uint32_t)i, (uint32_t)hi, (uint32_t)(bi + p.b0), p.seed_lo,
+                         p.seed_hi);
   return philox_word(w, j) >= p.drop_threshold ? p.drop_scale : 0.0f;
 }
 
@@ -449,6 +451,7 @@ bool generic_head_size(int d) { return d == 32 || d == 64 || d == 96 || d == 128
 hipError_t launch_fwd_generic(const FwdArgs& a, int elem, hipStream_t s) {
   GParams p = base_params(a.H, a.N, a.scale, a.causal, a.key_lens, a.dropout_p, a.drop_threshold,
                           a.drop_scale, a.seed);
+  p.b0 = a.b0;
   p.q = a.q;
   p.k = a.k;
   p.v = a.v;
@@ -465,6 +468,7 @@ hipError_t launch_fwd_generic(const FwdArgs& a, int elem, hipStream_t s) {
 hipError_t launch_bwd_generic(const BwdArgs& a, int elem, int stages, hipStream_t s) {
   GParams p = base_params(a.H, a.N, a.scale, a.causal, a.key_lens, a.dropout_p, a.drop_threshold,
                           a.drop_scale, a.seed);
+  p.b0 = a.b0;
   p.q = a.q;
   p.k = a.k;
   p.v = a.v;

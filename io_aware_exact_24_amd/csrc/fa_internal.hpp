@@ -32,6 +32,7 @@ struct FwdArgs {
   uint32_t drop_threshold;  // floor(p * 2^32)
   float drop_scale;         // fp32(1 / (1 - p))
   uint64_t seed;
+  int b0 = 0;  // batch index of entry 0 in the dropout counter (packed sequences)
   // Split-KV (bf16 only): num_splits > 0 splits each query block's key tiles
   // that many ways into the fp32 workspaces opart [S][B*H][N][d] and
   // lsepart [S][B*H][N], then combines them into o and lse.  0: one pass.
@@ -60,6 +61,7 @@ struct BwdArgs {
   uint32_t drop_threshold;
   float drop_scale;
   uint64_t seed;
+  int b0 = 0;  // batch index of entry 0 in the dropout counter (packed sequences)
   float* delta;   // workspace: fp32 [B, H, N], D_i = sum_k dO_ik O_ik
   float* lse2;    // workspace: fp32 [B, H, N], LSE_i * log2(e) (+inf for an empty row)
 };

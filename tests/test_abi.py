@@ -342,3 +342,59 @@ def test_fp16_is_a_16_bit_type_everywhere(lib):
     assert fwd_s(lib, rows, dtype=f16) == INVALID
     # fp32 rows: units of 4 elements
     assert fwd_s_accepts(lib, rows)
+
+
+# ---- fa_fwd_varlen / fa_bwd_varlen: packed sequences (host offsets)
+
+
+def cu_arr(vals):
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def fwd_v(lib, cu, H=2, d=64, dtype=binding.FA_BF16, p=0.0, strides=None, ptrs=None):
+    ptrs = ptrs or [P] * 5
+    n = len(cu) - 1 if cu is not None else 1
+    return lib.fa_fwd_varlen(*ptrs, strides, cu_arr(cu) if cu is not None else None, n, H, d, dtype,
+                             0.125, 0, p, 0, None)
+
+
+def test_varlen_rejects_bad_offsets(lib):
+    assert fwd_v(lib, None) == INVALID                 # no offsets
+    assert lib.fa_fwd_varlen(*([P] * 5), None, cu_arr([0]), 0, 2, 64, binding.FA_BF16, 0.125, 0,
+                             0.0, 0, None) == INVALID  # no sequence
+    assert fwd_v(lib, [3, 10]) == INVALID              # must start at 0
+    assert fwd_v(lib, [0, 10, 5]) == INVALID           # must not decrease
+    assert fwd_v(lib, [0, 10], d=48) == UNSUPPORTED
+    assert fwd_v(lib, [0, 10], dtype=7) == INVALID
+    assert fwd_v(lib, [0, 10], ptrs=[P, P, P, P + 8, P]) == INVALID  # o misaligned
+    # LSE needs 4-byte alignment only (sequence blocks start at H * offset);
+    # accepted here, then fp32 + dropout is the first check to fail
+    assert fwd_v(lib, [0, 3, 10], ptrs=[P, P, P, P, P + 4], dtype=binding.FA_F32, p=0.1) == UNSUPPORTED
+    assert fwd_v(lib, [0, 3, 10], ptrs=[P, P, P, P, P + 2]) == INVALID
+
+
+def test_varlen_strides_are_checked_over_all_tokens(lib):
+    T, H, d = 40, 2, 64
+    packed = (0, d, H * d)
+    good = strides_arr([packed] * 4)
+    assert fwd_v(lib, [0, 15, 40], strides=good, dtype=binding.FA_F32, p=0.1) == UNSUPPORTED
+    # o rows 64 apart with 2 heads: heads overlap the next token's rows
+    bad = strides_arr([packed] * 3 + [(0, d, d)])
+    assert fwd_v(lib, [0, 15, 40], strides=bad) == INVALID
+    # only empty sequences: no token, nothing to check against, nothing launched
+    assert fwd_v(lib, [0, 0, 0], strides=bad) == OK
+
+
+def test_varlen_backward_workspace_and_rejects(lib):
+    ws = lib.fa_bwd_varlen_workspace_size
+    # the per-row terms of the longest sequence, reused by the others
+    assert ws(cu_arr([0, 100, 130, 380]), 3, 2, 64, binding.FA_BF16) == \
+        lib.fa_bwd_workspace_size(1, 2, 250, 64, binding.FA_BF16)
+    assert ws(cu_arr([0, 0]), 1, 2, 64, binding.FA_BF16) == 0
+    assert ws(cu_arr([2, 5]), 1, 2, 64, binding.FA_BF16) == 0
+    need = ws(cu_arr([0, 100, 130]), 2, 2, 64, binding.FA_BF16)
+    call = lambda cu, dt=binding.FA_BF16, wsb=need, p=0.0: lib.fa_bwd_varlen(
+        *([P] * 9), None, cu_arr(cu), len(cu) - 1, 2, 64, dt, 0.125, 0, p, 0, P, wsb, None)
+    assert call([0, 100, 130], wsb=need - 1) == INVALID
+    assert call([0, 100, 90]) == INVALID
+    assert call([0, 100, 130], dt=binding.FA_F32, p=0.1) == UNSUPPORTED
