@@ -129,6 +129,48 @@ def cpu_baseline(w, heads=CPU_SAMPLE_HEADS):
     }
 
 
+def oracle_report():
+    """Wall time of the oracle, as it stands, on every workload (one JSON line
+    each): forward, then backward, one warm run each, on the host cores.  The
+    long causal workload is timed on the 64 sampled query rows its parity test
+    checks (O, LSE and dQ of those rows), and says so.  Needs no GPU."""
+    from io_aware_exact_24_amd.workloads import DROPOUT_SEED, WORKLOADS, draw_workload, sampled_rows
+    from oracle import attention_backward, attention_forward
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    model, blas = host_description()
+    for n, w in sorted(WORKLOADS.items()):
+        inp = draw_workload(w)
+        kl = None if inp.key_lens is None else inp.key_lens.tolist()
+        seed = DROPOUT_SEED if w.dropout_p > 0 else 0
+        kw = {}
+        what = "whole workload"
+        if w.N > 16384:
+            rows = sampled_rows(w.N, w.seed)
+            kw = dict(rows=rows, row_chunk=16)
+            what = f"{len(rows)} sampled query rows of every head (O, LSE; dQ of those rows)"
+        t0 = time.perf_counter()
+        attention_forward(inp.q, inp.k, inp.v, w.scale, w.causal, kl, w.dropout_p, seed, **kw)
+        tf = time.perf_counter() - t0
+        tb = None
+        if w.backward:
+            bkw = dict(q_rows=kw["rows"], k_rows=[], row_chunk=16) if kw else {}
+            t0 = time.perf_counter()
+            attention_backward(inp.q, inp.k, inp.v, inp.dout, w.scale, w.causal, kl, w.dropout_p,
+                               seed, **bkw)
+            tb = time.perf_counter() - t0
+        print(json.dumps({"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                          "oracle_fwd_s": round(tf, 2),
+                          "oracle_bwd_s": None if tb is None else round(tb, 2),
+                          "computed": what, "threads": threads, "cpu_model": model,
+                          "blas": blas}), flush=True)
+        del inp
+
+
 def summarize_traffic(fetch_dir, write_dir, out_path):
     """Turn two rocprofv3 --pmc runs of `bench.py --calibrate-copy` (FETCH_SIZE,
     then WRITE_SIZE; KiB per dispatch) into HBM bytes per launch of each
@@ -157,8 +199,9 @@ def summarize_traffic(fetch_dir, write_dir, out_path):
     w_scale = true_kib / (sum(write[copy[0]]) / len(write[copy[0]]))
     rows = []
     for k in sorted(fetch):
-        m = re.search(r"(\w+_kernel)", k)
-        if not m or "fa::" not in k or k not in write or m.group(1) not in KERNEL_SOURCES:
+        # demangled ("fa::...::fwd_kernel<...>") or mangled ("_ZN2fa...10fwd_kernelI...")
+        m = re.search(r"(?<![A-Za-z_])(" + "|".join(KERNEL_SOURCES) + r")(?=I|<|\b)", k)
+        if not m or not ("fa::" in k or k.startswith("_ZN2fa")) or k not in write:
             continue
         fk = sum(fetch[k]) / len(fetch[k]) * f_scale * 1024
         wk = sum(write[k]) / len(write[k]) * w_scale * 1024
@@ -278,6 +321,9 @@ def all_configs(steps, warmup):
 
 
 def main():
+    if len(sys.argv) == 2 and sys.argv[1] == "--oracle-report":
+        oracle_report()
+        return
     if len(sys.argv) == 4 and sys.argv[1] == "--summarize-traffic":
         summarize_traffic(sys.argv[2], sys.argv[3],
                           os.path.join(ROOT, "profiles", "traffic_decoder_causal.md"))
