@@ -269,6 +269,53 @@ def unmasked_pairs(w, key_lens):
     return w.B * w.H * w.N * w.N
 
 
+def split_sweep(shape, counts):
+    """Back-to-back times (back_to_back_ms) of the plain and the split passes on
+    one bf16 shape B,H,N,d,causal: fa_fwd and fa_fwd_split, fa_bwd and
+    fa_bwd_split, for each split count; one JSON line.  A report for choosing
+    split counts, not the metric line."""
+    import torch
+
+    from io_aware_exact_24_amd import autograd, binding
+    from io_aware_exact_24_amd.workloads import draw
+
+    B, H, N, d, causal = shape
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    inp = draw(B, H, N, d, torch.bfloat16, seed=4242)
+    q, k, v, do = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.dout))
+    scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(binding.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+    rec = {"shape": {"B": B, "H": H, "N": N, "d": d, "causal": bool(causal)}, "fwd_ms": {},
+           "bwd_ms": {}}
+    rec["fwd_ms"]["0"] = round(back_to_back_ms(
+        lambda: binding.fa_fwd(q, k, v, o, lse, scale, causal, None, 0.0, 0, stream), stream), 4)
+    rec["bwd_ms"]["0"] = round(back_to_back_ms(
+        lambda: binding.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, None, 0.0, 0, ws,
+                               stream), stream), 4)
+    for s in counts:
+        fws = torch.empty(binding.fa_fwd_split_workspace_size(B, H, N, d, s), dtype=torch.uint8,
+                          device=dev)
+        rec["fwd_ms"][str(s)] = round(back_to_back_ms(
+            lambda: binding.fa_fwd_split(q, k, v, o, lse, scale, causal, None, 0.0, 0, s, fws,
+                                         stream), stream), 4)
+        del fws
+        bws = torch.empty(binding.fa_bwd_split_workspace_size(B, H, N, d, s), dtype=torch.uint8,
+                          device=dev)
+        rec["bwd_ms"][str(s)] = round(back_to_back_ms(
+            lambda: binding.fa_bwd_split(q, k, v, o, do, lse, dq, dk, dv, scale, causal, None, 0.0,
+                                         0, s, bws, stream), stream), 4)
+        del bws
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    rec["chosen"] = {"fwd": autograd.split_count(B, H, N, d, bool(causal), cus),
+                     "bwd": autograd.backward_split_count(B, H, N, d, bool(causal), cus)}
+    print(json.dumps(rec), flush=True)
+
+
 def all_configs(steps, warmup):
     """Time fa_fwd and fa_bwd on every workload (one JSON line each): inputs
     resident on the GPU, back-to-back calls on the library's stream timed by
@@ -338,6 +385,11 @@ def main():
                          "baseline)")
     ap.add_argument("--splits", type=int, default=0,
                     help="run the forward as fa_fwd_split with this many key splits")
+    ap.add_argument("--split-sweep", default=None, metavar="B,H,N,d,causal",
+                    help="time fa_fwd/fa_fwd_split and fa_bwd/fa_bwd_split on one bf16 shape for "
+                         "the split counts of --split-counts instead")
+    ap.add_argument("--split-counts", default="2,4,8,16",
+                    help="comma-separated split counts for --split-sweep")
     ap.add_argument("--all-configs", action="store_true",
                     help="time forward and backward on every workload (one JSON line each) instead")
     ap.add_argument("--step-only", action="store_true",
@@ -354,6 +406,12 @@ def main():
 
     if args.all_configs:
         all_configs(args.steps, args.warmup)
+        return
+    if args.split_sweep:
+        f = [int(x) for x in args.split_sweep.split(",")]
+        if len(f) != 5:
+            raise SystemExit("--split-sweep takes B,H,N,d,causal")
+        split_sweep(f, [int(x) for x in args.split_counts.split(",")])
         return
 
     import torch

@@ -260,6 +260,37 @@ fa_status fa_bwd_strided(const void* q, const void* k, const void* v, const void
                          hipStream_t stream);
 
 /*
+ * Split backward, for shapes whose B * H leaves CUs idle (Flash Attention
+ * hardware-aware optimisation, section 4: FlashAttention-2 spreads the work
+ * over the sequence as well as over batch and heads).  fa_bwd launches one
+ * workgroup per 128-query block for dQ and one work unit per 128-key block
+ * (a causal pair of them) for dK/dV; here each of those is cut into
+ * num_splits shares: dQ's workgroups take shares of a block's key tiles, and
+ * dK/dV's units take shares of a block's query tiles (with a causal pair, of
+ * the tiles of both blocks in turn, so the shares are equal).  Each share
+ * writes fp32 partial rows to the workspace, and a combine pass sums them
+ * into dq, dk and dv.
+ *
+ *   num_splits   1 .. FA_MAX_SPLITS (else FA_ERR_INVALID_ARG); shares
+ *                without a tile are allowed and contribute zeros.
+ *   workspace    device buffer of at least fa_bwd_split_workspace_size()
+ *                bytes: fa_bwd's per-row terms plus three fp32
+ *                [num_splits, B, H, N, d] partial arrays, each padded to a
+ *                multiple of 256 bytes; 16-byte aligned, contents irrelevant
+ *                on entry, garbage on exit.
+ * Everything else as fa_bwd, for contiguous tensors and the MFMA kernels only
+ * (FA_BF16 / FA_F16 at d in {64, 128}, else FA_ERR_UNSUPPORTED).  The result
+ * is deterministic; with num_splits = 1 it equals fa_bwd's bit for bit, with
+ * more shares up to rounding (the partial sums are added in another order).
+ */
+size_t fa_bwd_split_workspace_size(int B, int H, int N, int d, fa_dtype dtype, int num_splits);
+fa_status fa_bwd_split(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                       const int32_t* key_lens, float dropout_p, uint64_t seed, int num_splits,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The backward in stages.  fa_bwd enqueues fa_bwd_dq, then fa_bwd_dkdv, on its
  * stream; they are exported so that a caller can time them, or compute dK/dV
  * alone (fa_bwd_preprocess, then fa_bwd_dkdv).  Arguments have the meaning

@@ -2,9 +2,9 @@
 
 `flash_attention` runs fa_fwd (fa_fwd_split when the shape has too few query
 blocks to fill the GPU) in the forward of a torch.autograd.Function and fa_bwd
-in its backward, keeping only what the recompute backward needs: Q, K,
-V, O and the per-row log-sum-exp (no N x N matrix; ML Canon 48 FlashAttention,
-"backward without N x N").  `scaled_dot_product_attention` takes the argument
+(fa_bwd_split when it has too few key blocks) in its backward, keeping only
+what the recompute backward needs: Q, K, V, O and the per-row log-sum-exp (no
+N x N matrix; ML Canon 48 FlashAttention, "backward without N x N").  `scaled_dot_product_attention` takes the argument
 names of torch.nn.functional.scaled_dot_product_attention, the drop-in call the
 same page shows, for the cases the library computes.
 
@@ -63,6 +63,31 @@ def split_count(B, H, N, d, causal, cus):
     return s if s >= 2 else 0
 
 
+def backward_split_count(B, H, N, d, causal, cus):
+    """Shares for the backward of one shape (0: the plain fa_bwd).
+
+    The dK/dV stage runs one persistent workgroup per CU over work units of
+    one 128-key block (with a causal mask, a pair of blocks of equal total
+    work).  When there are fewer units than CUs, fa_bwd_split cuts each
+    unit's query tiles (and each query block's key tiles for dQ) into enough
+    shares for one unit per CU, at least 2, capped so that every share keeps
+    at least four 64-row tiles and at FA_MAX_SPLITS.  Only the MFMA head sizes
+    have a split backward.
+    """
+    if d not in (64, 128):
+        return 0
+    blocks = (N + 127) // 128
+    units = B * H * ((blocks + 1) // 2 if causal else blocks)
+    if units >= cus:
+        return 0
+    tiles = (N + 63) // 64
+    per_unit = tiles + 2 if causal else tiles  # a causal pair's tiles, both blocks
+    want = max(2, -(-cus // units))
+    cap = min(max(per_unit // 4, 1), binding.FA_MAX_SPLITS)
+    s = min(want, cap)
+    return s if s >= 2 else 0
+
+
 def _splits(q, causal):
     """split_count for q's shape on its GPU: 16-bit types, contiguous tensors
     only (the split entry point takes no strides)."""
@@ -80,6 +105,18 @@ def _forward(q, k, v, scale, causal, key_lens, dropout_p, seed):
     return binding.forward(q, k, v, scale, causal, key_lens, dropout_p, seed)
 
 
+def _bwd_splits(q, causal, tensors):
+    """backward_split_count for q's shape on its GPU: 16-bit types, every
+    tensor contiguous (the split entry point takes no strides)."""
+    if q.dtype not in (torch.bfloat16, torch.float16) or not q.is_cuda:
+        return 0
+    if not all(t.is_contiguous() for t in tensors):
+        return 0
+    B, H, N, d = q.shape
+    cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+    return backward_split_count(B, H, N, d, causal, cus)
+
+
 class FlashAttentionFunction(torch.autograd.Function):
     """O = softmax(mask(scale * Q K^T)) (with dropout) V on [B, H, N, d]."""
 
@@ -95,8 +132,14 @@ class FlashAttentionFunction(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
         scale, causal, dropout_p, seed = ctx.args
-        dq, dk, dv = binding.backward(q, k, v, o, _in_place(do), lse, scale, causal,
-                                      ctx.key_lens, dropout_p, seed)
+        do = _in_place(do)
+        s = _bwd_splits(q, causal, (q, k, v, o, do))
+        if s:
+            dq, dk, dv = binding.backward_split(q, k, v, o, do, lse, scale, causal, ctx.key_lens,
+                                                dropout_p, seed, s)
+        else:
+            dq, dk, dv = binding.backward(q, k, v, o, do, lse, scale, causal, ctx.key_lens,
+                                          dropout_p, seed)
         return dq, dk, dv, None, None, None, None, None
 
 

@@ -19,7 +19,7 @@ FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_split", "fa_fwd_split_workspace_size",
            "fa_bwd_noalloc", "fa_fwd_strided", "fa_bwd_strided", "fa_fwd_varlen", "fa_bwd_varlen",
-           "fa_bwd_varlen_workspace_size")
+           "fa_bwd_varlen_workspace_size", "fa_bwd_split", "fa_bwd_split_workspace_size")
 FA_MAX_SPLITS = 64
 FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -60,6 +60,11 @@ def load_library():
     lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f, u64, i, vp, sz, vp]
     lib.fa_fwd_split_workspace_size.restype = sz
     lib.fa_fwd_split_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.fa_bwd_split.restype = i
+    lib.fa_bwd_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, f,
+                                 u64, i, vp, sz, vp]
+    lib.fa_bwd_split_workspace_size.restype = sz
+    lib.fa_bwd_split_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -269,6 +274,49 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None
                     _stream(stream, q.device))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def fa_bwd_split_workspace_size(B, H, N, d, num_splits, dtype_code=FA_BF16):
+    return int(load_library().fa_bwd_split_workspace_size(B, H, N, d, dtype_code, num_splits))
+
+
+def fa_bwd_split(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None,
+                 dropout_p=0.0, seed=0, num_splits=2, workspace=None, stream=None):
+    """Enqueue the split backward (16-bit, contiguous); dq, dk, dv are written.
+    workspace: a uint8 device tensor of at least fa_bwd_split_workspace_size()
+    bytes."""
+    import torch
+
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, q.shape, q.dtype, q.device, name)
+    _check(q, q.shape, q.dtype, q.device, "q")
+    _check(lse, (B, H, N), torch.float32, q.device, "lse")
+    kl = _key_lens(key_lens, B, q.device)
+    if workspace is None:
+        raise ValueError("fa_bwd_split needs a workspace tensor (see fa_bwd_split_workspace_size)")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_bwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                          _ptr(dk), _ptr(dv), B, H, N, d, _dtype_code(q), float(scale),
+                          int(bool(causal)), _ptr(kl), float(dropout_p), int(seed),
+                          int(num_splits), _ptr(workspace), ws_bytes, _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_split")
+
+
+def backward_split(q, k, v, o, dout, lse, scale, causal=False, key_lens=None, dropout_p=0.0, seed=0,
+                   num_splits=2, stream=None):
+    """Allocate dQ, dK, dV and the workspace with torch and call fa_bwd_split."""
+    import torch
+
+    B, H, N, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = fa_bwd_split_workspace_size(B, H, N, d, num_splits, _dtype_code(q))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    fa_bwd_split(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, key_lens, dropout_p, seed,
+                 num_splits, ws, stream)
+    return dq, dk, dv
 
 
 def fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, scale, causal=False, key_lens=None,

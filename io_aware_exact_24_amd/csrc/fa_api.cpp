@@ -255,7 +255,8 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, const fa_strides* strides, int B,
                   int H, int N, int d, fa_dtype dtype, float scale, int causal,
                   const int32_t* key_lens, float dropout_p, uint64_t seed, void* workspace,
-                  int stages, hipStream_t stream, int b0 = 0) {
+                  int stages, hipStream_t stream, int b0 = 0, int num_splits = 0,
+                  float* dqp = nullptr, float* dkp = nullptr, float* dvp = nullptr) {
   fa::BwdArgs a;
   a.fp16 = dtype == FA_F16;
   a.q = q;
@@ -282,6 +283,10 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   // workspace: D, then LSE * log2(e)
   a.delta = (float*)workspace;
   a.lse2 = (float*)((char*)workspace + row_array_bytes(B, H, N));
+  a.num_splits = num_splits;
+  a.dqp = dqp;
+  a.dkp = dkp;
+  a.dvp = dvp;
   fa::Strides* dst[8] = {&a.sq, &a.sk, &a.sv, &a.so, &a.sdo, &a.sdq, &a.sdk, &a.sdv};
   for (int t = 0; t < 8; ++t) *dst[t] = to_strides(strides ? &strides[t] : nullptr, H, N, d);
   const hipError_t e = mfma_path(dtype, d) ? fa::launch_bwd_16(a, stages, stream)
@@ -360,6 +365,35 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, 
   if (st != FA_OK) return st;
   return run_bwd(q, k, v, o, dout, lse, dq, nullptr, nullptr, nullptr, B, H, N, d, dtype, scale,
                  causal, key_lens, dropout_p, seed, workspace, fa::kBwdQ, stream);
+}
+
+size_t fa_bwd_split_workspace_size(int B, int H, int N, int d, fa_dtype dtype, int num_splits) {
+  if (elems(B, H, N, d) < 0 || !mfma_path(dtype, d) || num_splits < 1 ||
+      num_splits > FA_MAX_SPLITS || !head_bytes_fit(N, d, dtype))
+    return 0;
+  const size_t part = pad256((size_t)num_splits * B * H * N * d * 4);
+  return fa_bwd_workspace_size(B, H, N, d, dtype) + 3 * part;
+}
+
+fa_status fa_bwd_split(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                       int H, int N, int d, fa_dtype dtype, float scale, int causal,
+                       const int32_t* key_lens, float dropout_p, uint64_t seed, int num_splits,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_INVALID_ARG;
+  fa_status st = check_bwd({q, k, v, o, dout, dq, dk, dv}, lse, B, H, N, d, dtype, scale,
+                           dropout_p, workspace, workspace_bytes, key_lens);
+  if (st != FA_OK) return st;
+  if (!mfma_path(dtype, d)) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa_bwd_split_workspace_size(B, H, N, d, dtype, num_splits))
+    return FA_ERR_INVALID_ARG;
+  // workspace: D, LSE * log2(e), then the partial dQ, dK and dV rows
+  const size_t base = fa_bwd_workspace_size(B, H, N, d, dtype);
+  const size_t part = pad256((size_t)num_splits * B * H * N * d * 4);
+  char* ws = (char*)workspace;
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, nullptr, B, H, N, d, dtype, scale, causal,
+                 key_lens, dropout_p, seed, workspace, fa::kBwdAll, stream, 0, num_splits,
+                 (float*)(ws + base), (float*)(ws + base + part), (float*)(ws + base + 2 * part));
 }
 
 }  // extern "C"

@@ -32,6 +32,11 @@ hipError_t launch_bwd_16(const BwdArgs& a, int stages, hipStream_t s) {
   p.b0 = a.b0;
   p.num_blocks = 0;
   p.units = 0;
+  p.heads = a.B * a.H;
+  p.splits = a.num_splits;
+  p.dqp = a.num_splits > 0 && (stages & kBwdQ) ? a.dqp : nullptr;
+  p.dkp = a.num_splits > 0 && (stages & kBwdKV) ? a.dkp : nullptr;
+  p.dvp = a.num_splits > 0 && (stages & kBwdKV) ? a.dvp : nullptr;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   p.drop_threshold = a.drop_threshold;
@@ -52,8 +57,30 @@ hipError_t launch_bwd_16(const BwdArgs& a, int stages, hipStream_t s) {
     const hipError_t e = launch_bwd_dq(p, a.fp16, a.d, causal, dropout, contig, heads, s);
     if (e != hipSuccess) return e;
   }
-  if (stages & kBwdKV) return launch_bwd_dkdv(p, a.fp16, a.d, causal, dropout, contig, heads, s);
+  if (stages & kBwdKV) {
+    const hipError_t e = launch_bwd_dkdv(p, a.fp16, a.d, causal, dropout, contig, heads, s);
+    if (e != hipSuccess) return e;
+  }
+  if (a.num_splits > 0 && (stages & (kBwdQ | kBwdKV)))
+    return launch_bwd_combine(p, a.fp16, a.d, (int64_t)heads * a.N, s);
   return hipSuccess;
+}
+
+namespace {
+
+template <typename E, int D>
+hipError_t combine_d(const BwdParams& p, int64_t rows, hipStream_t s) {
+  const int64_t threads = rows * (D / 8);
+  hipLaunchKernelGGL((bwd_combine_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     s, p, rows);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_combine(const BwdParams& p, bool fp16, int d, int64_t rows, hipStream_t s) {
+  if (fp16) return d == 64 ? combine_d<f16, 64>(p, rows, s) : combine_d<f16, 128>(p, rows, s);
+  return d == 64 ? combine_d<bf16, 64>(p, rows, s) : combine_d<bf16, 128>(p, rows, s);
 }
 
 }  // namespace fa

@@ -6,28 +6,34 @@
 namespace fa {
 namespace {
 
-template <typename E, int D, bool CAUSAL, bool DROPOUT, bool CONTIG>
+template <typename E, int D, bool CAUSAL, bool DROPOUT, bool CONTIG, bool SPLIT>
 hipError_t launch_dq(BwdParams p, int heads, hipStream_t s) {
   p.num_blocks = (p.N + QCfg<D>::BM - 1) / QCfg<D>::BM;
   const int per_head = CAUSAL ? (p.num_blocks + 1) / 2 : p.num_blocks;
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, DROPOUT, CONTIG>), dim3(heads * per_head),
+  const int64_t grid = (int64_t)heads * per_head * (SPLIT ? p.splits : 1);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, DROPOUT, CONTIG, SPLIT>), dim3((unsigned)grid),
                      dim3(QCfg<D>::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
-template <typename E, int D, bool CONTIG>
+// The split kernels exist for contiguous rows only.
+template <typename E, int D, bool CONTIG, bool SPLIT>
 hipError_t dq_flags(const BwdParams& p, bool causal, bool dropout, int heads, hipStream_t s) {
   if (causal)
-    return dropout ? launch_dq<E, D, true, true, CONTIG>(p, heads, s)
-                   : launch_dq<E, D, true, false, CONTIG>(p, heads, s);
-  return dropout ? launch_dq<E, D, false, true, CONTIG>(p, heads, s)
-                 : launch_dq<E, D, false, false, CONTIG>(p, heads, s);
+    return dropout ? launch_dq<E, D, true, true, CONTIG, SPLIT>(p, heads, s)
+                   : launch_dq<E, D, true, false, CONTIG, SPLIT>(p, heads, s);
+  return dropout ? launch_dq<E, D, false, true, CONTIG, SPLIT>(p, heads, s)
+                 : launch_dq<E, D, false, false, CONTIG, SPLIT>(p, heads, s);
 }
 
 template <typename E, int D>
 hipError_t dq_d(const BwdParams& p, bool causal, bool dropout, bool contig, int heads, hipStream_t s) {
-  return contig ? dq_flags<E, D, true>(p, causal, dropout, heads, s)
-                : dq_flags<E, D, false>(p, causal, dropout, heads, s);
+  if (p.splits > 0) {
+    if (!contig) return hipErrorInvalidValue;
+    return dq_flags<E, D, true, true>(p, causal, dropout, heads, s);
+  }
+  return contig ? dq_flags<E, D, true, false>(p, causal, dropout, heads, s)
+                : dq_flags<E, D, false, false>(p, causal, dropout, heads, s);
 }
 
 template <typename E, int D>

@@ -66,7 +66,16 @@ struct BwdParams {
   const int32_t* key_lens;
   int H, N, num_blocks;
   int b0;  // added to the batch index in the dropout counter
-  int units;  // dK/dV work units (blocks, or causal pairs of blocks) over all heads
+  int units;  // dK/dV work units (blocks, or causal pairs of blocks, times splits) over all heads
+  int heads;  // B * H
+  // Split backward: `splits` shares per query block (dQ: of its key tiles) or
+  // per key-block unit (dK/dV: of its query tiles); share s writes its fp32
+  // partial gradient rows to dqp / dkp / dvp + ((s * heads + head) * N + row) * d,
+  // every row of its blocks (zeros where the share has no tile).
+  int splits;
+  float* dqp;
+  float* dkp;
+  float* dvp;
   float scale, scale_log2;
   uint32_t drop_threshold;
   float drop_scale;
@@ -80,6 +89,9 @@ hipError_t launch_bwd_dq(BwdParams p, bool fp16, int d, bool causal, bool dropou
                          int heads, hipStream_t s);
 hipError_t launch_bwd_dkdv(BwdParams p, bool fp16, int d, bool causal, bool dropout, bool contig,
                            int heads, hipStream_t s);
+// Split backward (p.splits > 0, contiguous rows): the same two stages writing
+// fp32 partials, then the combine pass into dq, dk, dv.
+hipError_t launch_bwd_combine(const BwdParams& p, bool fp16, int d, int64_t rows, hipStream_t s);
 
 namespace {
 
@@ -149,7 +161,7 @@ __device__ __forceinline__ uint32_t quad_keep4(const BwdParams& p, int row0, int
 //   phase 3: dP_{t+1} = dO_{t+1} V^T  | P_{t+1} of rows 32..63
 // Tiles t (transposing reads) and t+1 (row reads) are read while tile t+2 is
 // copied, so Q, dO, LSE*log2e and D have three LDS stages.
-template <typename E, int D, bool CAUSAL, bool DROPOUT, bool CONTIG>
+template <typename E, int D, bool CAUSAL, bool DROPOUT, bool CONTIG, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p) {
   using C = KvCfg<D>;
@@ -204,6 +216,10 @@ void bwd_dkdv_kernel(BwdParams p) {
   // Q/dO tiles then stay in that XCD's L2), dealt round-robin to its
   // workgroups, and a workgroup walks its blocks as one chain, fetching the
   // next block's K and V rows while it works on the current one.
+  // SPLIT: a unit is (block or causal pair, share s); the unit's query tiles
+  // (with a pair, those of its first block followed by those of its second)
+  // are divided into p.splits nearly equal shares, and share s visits each
+  // block of the unit with its part of them (possibly none).
   const int per_head = CAUSAL ? (nb + 1) / 2 : nb;
   const int G = gridDim.x;
   int u, ustep, uend;
@@ -219,10 +235,12 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
   int sub = 0;  // which block of the unit
   auto block_of = [&](int uu, int ss, int& head_, int& jb_) {
-    head_ = uu / per_head;
-    const int w = uu - head_ * per_head;
+    const int pu = SPLIT ? uu / p.splits : uu;
+    head_ = pu / per_head;
+    const int w = pu - head_ * per_head;
     jb_ = ss == 0 ? w : nb - 1 - w;
   };
+  const int nit = (N + BQ - 1) / BQ;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
@@ -235,8 +253,29 @@ void bwd_dkdv_kernel(BwdParams p) {
   started = true;
   int head, jb;
   block_of(u, sub, head, jb);
+  // Query tiles [tlo, thi) of this visit.
+  int tlo = CAUSAL ? jb * (BK / BQ) : 0, thi = nit;
+  if constexpr (SPLIT) {
+    const int s = u % p.splits, w = (u / p.splits) % per_head;
+    if constexpr (CAUSAL) {
+      const int wb = nb - 1 - w;
+      const int na = nit - w * (BK / BQ), nbt = wb != w ? nit - wb * (BK / BQ) : 0;
+      const int lo = (na + nbt) * s / p.splits, hi = (na + nbt) * (s + 1) / p.splits;
+      if (sub == 0) {
+        tlo = w * (BK / BQ) + min(lo, na);
+        thi = w * (BK / BQ) + min(hi, na);
+      } else {
+        tlo = wb * (BK / BQ) + max(lo - na, 0);
+        thi = wb * (BK / BQ) + max(hi - na, 0);
+      }
+    } else {
+      tlo = nit * s / p.splits;
+      thi = nit * (s + 1) / p.splits;
+    }
+  }
+  const int share = SPLIT ? u % p.splits : 0;
   {
-    const int w = u % per_head;
+    const int w = (SPLIT ? u / p.splits : u) % per_head;
     if (CAUSAL && sub == 0 && w != nb - 1 - w) {
       sub = 1;
     } else {
@@ -266,9 +305,19 @@ void bwd_dkdv_kernel(BwdParams p) {
   // Keys past the key length take part in nothing: their gradients are zero.
   // Their lanes compute unmasked values (each lane's columns of S, dP, dV^T
   // and dK^T depend on its own key only), which the epilogue replaces by zeros.
-  if (kb >= L) {  // every key of the block is padding
+  // SPLIT: partial rows of fp32 zeros also for a visit without query tiles.
+  float* const dkpart = SPLIT ? p.dkp + (((size_t)share * p.heads + head) * N + key) * D : nullptr;
+  float* const dvpart = SPLIT ? p.dvp + (((size_t)share * p.heads + head) * N + key) * D : nullptr;
+  if (kb >= L || (SPLIT && tlo >= thi)) {  // every key of the block is padding, or no tile
     prefetched = false;  // the next block's rows are fetched at its start
-    if (key < N) {
+    if (SPLIT && key < N) {
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < D / 4; c += 2) {
+        *(f32x4*)(dkpart + 4 * c + 4 * hh) = z;
+        *(f32x4*)(dvpart + 4 * c + 4 * hh) = z;
+      }
+    } else if (key < N) {
       const V4 z = {(E)0.0f, (E)0.0f, (E)0.0f, (E)0.0f};
 #pragma unroll
       for (int c = 0; c < D / 4; c += 2) {
@@ -405,8 +454,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   };
 
   const float c2 = p.scale_log2;
-  const int it0 = CAUSAL ? kb / BQ : 0;
-  const int nit = (N + BQ - 1) / BQ;
+  const int it0 = tlo;  // the first query tile (with a causal mask, a diagonal one unless SPLIT)
 
   // State carried from one tile to the next: P (fp32, masked), dP, P~ packed
   // as B chunks (chunk kc holds rows 16kc + 8(x/4) + 4hh + x%4 in slot x), the
@@ -507,7 +555,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
 
   // ---- one tile: t in stage S, t+1 in stage S+1.  The body after the last
-  // tile also computes S, dP and P of a tile t+1 = nit, from whatever its
+  // tile also computes S, dP and P of a tile t+1 = thi, from whatever its
   // stage holds; the loop ends before anything reads them.
   auto body = [&](int t, auto s_t, auto mask_next_t, auto first_t) __attribute__((always_inline)) {
     constexpr int S = decltype(s_t)::value;
@@ -618,15 +666,16 @@ void bwd_dkdv_kernel(BwdParams p) {
   };
 
   // With a causal mask the block's diagonal spans its first two tiles: the
-  // prologue masks the first, the first body the second.
+  // prologue masks the first, the first body the second.  (A split visit
+  // starting past them masks nothing there.)
   using CausalT = std::integral_constant<bool, CAUSAL>;
   body(it0, Stage<0>{}, CausalT{}, T_{});
   for (int t = it0 + 1;; t += 3) {
-    if (t >= nit) break;
+    if (t >= thi) break;
     body(t, Stage<1>{}, F_{}, F_{});
-    if (t + 1 >= nit) break;
+    if (t + 1 >= thi) break;
     body(t + 1, Stage<2>{}, F_{}, F_{});
-    if (t + 2 >= nit) break;
+    if (t + 2 >= thi) break;
     body(t + 2, Stage<0>{}, F_{}, F_{});
   }
   // the last accumulate MFMAs complete before the VALU reads dK^T and dV^T
@@ -638,9 +687,15 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
   // dK = scale * dK^T^T and dV through LDS (stages 0 and 1 are free once every
   // wave is past the last tile), then whole rows to memory.  Keys past the key
-  // length get zeros; rows past N are not written.
-  __syncthreads();
-  {
+  // length get zeros; rows past N are not written.  SPLIT: fp32 partial rows,
+  // straight from the accumulators.
+  if constexpr (SPLIT) {
+    if (key < N) {
+      acc_row_to_f32<D>(dkpart, dkacc, p.scale, key >= L, hh);
+      acc_row_to_f32<D>(dvpart, dvacc, 1.0f, key >= L, hh);
+    }
+  } else {
+    __syncthreads();
     const bool zero = key >= L;
     E* kt = ((wave >> 1) ? so0 : sq0) + (wave & 1) * 32 * D;
     E* vt = ((wave >> 1) ? so1 : sq1) + (wave & 1) * 32 * D;
@@ -669,7 +724,7 @@ struct QCfg {
   static_assert(LOADS * THREADS == BN * CHUNKS, "tile/thread mismatch");
 };
 
-template <typename E, int D, bool CAUSAL, bool DROPOUT, bool CONTIG>
+template <typename E, int D, bool CAUSAL, bool DROPOUT, bool CONTIG, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
   using C = QCfg<D>;
@@ -687,8 +742,15 @@ void bwd_dq_kernel(BwdParams p) {
   const int N = p.N;
   const int nqb = p.num_blocks;
   // Causal: a workgroup takes query blocks nqb-1-w and w in turn (equal work).
+  // SPLIT: p.splits workgroups per such unit, workgroup s taking share s of
+  // each block's key tiles and writing fp32 partial dQ rows.
   const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  int lid = xcd_remap(blockIdx.x, gridDim.x);
+  int share = 0;
+  if constexpr (SPLIT) {
+    share = lid % p.splits;
+    lid /= p.splits;
+  }
   const int head = lid / per_head;
   const int w = lid - head * per_head;
   const int nitems = CAUSAL && w != nqb - 1 - w ? 2 : 1;
@@ -824,7 +886,7 @@ void bwd_dq_kernel(BwdParams p) {
     lrow = lv == -INFINITY ? INFINITY : lv * kLog2e;
   }
   drow = pair_sum(drow);
-  if (hh == 0 && qi < N) {
+  if (hh == 0 && qi < N && share == 0) {
     p.delta[(size_t)head * N + qi] = drow;
     p.lse2[(size_t)head * N + qi] = lrow;
   }
@@ -939,30 +1001,41 @@ void bwd_dq_kernel(BwdParams p) {
     wait_vmem();
   };
 
-  if (nkb > 0) {
-    issue(0, P0{});
+  // Key tiles [jlo, jhi) of this workgroup (SPLIT: its share of [0, nkb)).
+  int jlo = 0, jhi = nkb;
+  if constexpr (SPLIT) {
+    jlo = nkb * share / p.splits;
+    jhi = nkb * (share + 1) / p.splits;
+  }
+  if (jlo < jhi) {
+    issue(jlo, P0{});
     wait_vmem();
   }
-  // Unmasked tiles first (from key 0), then the masked diagonal / tail ones.
-  // Steps run in pairs from even indices so the stage parity is a compile-time
+  // Unmasked tiles first (from key tile jlo), then the masked diagonal / tail
+  // ones.  Steps run in pairs from jlo so the stage parity is a compile-time
   // constant; tiles in [jm, nfree) take the masked path (harmless, it only
   // masks nothing there).
-  const int jm = nfree & ~1;
-  int j = 0;
+  const int jm = jlo + ((min(max(nfree, jlo), jhi) - jlo) & ~1);
+  int j = jlo;
   for (; j < jm; j += 2) {
     step(j, P0{}, F_{});
     step(j + 1, P1{}, F_{});
   }
-  for (; j + 1 < nkb; j += 2) {
+  for (; j + 1 < jhi; j += 2) {
     step(j, P0{}, T_{});
     step(j + 1, P1{}, T_{});
   }
-  if (j < nkb) step(j, P0{}, T_{});
+  if (j < jhi) step(j, P0{}, T_{});
 
   // dQ = scale * dQ^T^T, transposed through the K stages (free once every
-  // wave is past the last tile) and written as whole rows.
-  __syncthreads();
-  {
+  // wave is past the last tile) and written as whole rows.  SPLIT: fp32
+  // partial rows, straight from the accumulators (zeros without a tile).
+  if constexpr (SPLIT) {
+    if (qi < N)
+      acc_row_to_f32<D>(p.dqp + (((size_t)share * p.heads + head) * N + qi) * D, qacc, p.scale, false,
+                        hh);
+  } else {
+    __syncthreads();
     const int qw = q0 + wave * 32;
     E* qt = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
     acc_rows_to_lds<D, E>(qt, qacc, p.scale, false, li, hh);
@@ -998,6 +1071,40 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t rows)
     const float lv = p.lse[row];
     p.lse2[row] = lv == -INFINITY ? INFINITY : lv * kLog2e;
   }
+}
+
+// Split backward: dQ, dK and dV = the sums of the splits' fp32 partial rows,
+// converted to the element type and written through the output strides.  One
+// thread per 8 elements of a row.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwd_combine_kernel(BwdParams p, int64_t rows) {
+  typedef E v8 __attribute__((ext_vector_type(8)));
+  constexpr int LPR = D / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / LPR;
+  if (row >= rows) return;
+  const int ch = (int)(t % LPR);
+  const int head = (int)(row / p.N), n = (int)(row - (int64_t)head * p.N);
+  const int bi = head / p.H, hi = head - bi * p.H;
+  const size_t split_stride = (size_t)rows * D;
+  auto sum8 = [&](const float* part) {
+    f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f}, b = a;
+    const float* x = part + (size_t)row * D + ch * 8;
+    for (int s = 0; s < p.splits; ++s) {
+      a += *(const f32x4*)(x + s * split_stride);
+      b += *(const f32x4*)(x + s * split_stride + 4);
+    }
+    v8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (E)a[e];
+      r[4 + e] = (E)b[e];
+    }
+    return r;
+  };
+  if (p.dqp) *(v8*)((E*)p.dq + (bi * p.sdq.b + hi * p.sdq.h + (int64_t)n * p.sdq.n) + ch * 8) = sum8(p.dqp);
+  if (p.dkp) *(v8*)((E*)p.dk + (bi * p.sdk.b + hi * p.sdk.h + (int64_t)n * p.sdk.n) + ch * 8) = sum8(p.dkp);
+  if (p.dvp) *(v8*)((E*)p.dv + (bi * p.sdv.b + hi * p.sdv.h + (int64_t)n * p.sdv.n) + ch * 8) = sum8(p.dvp);
 }
 
 }  // namespace

@@ -277,8 +277,33 @@ __device__ __forceinline__ void acc_rows_to_lds(E* tile, const f32x16 (&acc)[D /
     for (int g = 0; g < 4; ++g) {
       v4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = zero ? (E)0.0f : (E)(acc[u][4 * g + e] * mul);
+      for (int e = 0; e < 4; ++e) {
+        // The product rounded to fp32, then converted: without the pin, fp16
+        // output may fuse both roundings into one mixed-precision FMA, and
+        // the result would depend on which kernel variant it came from.
+        float x = acc[u][4 * g + e] * mul;
+        pin(x);
+        v[e] = zero ? (E)0.0f : (E)x;
+      }
       *(v4*)(tile + li * D + (((4 * u + g) ^ swz<D>(li)) * 8) + 4 * hh) = v;
+    }
+}
+
+// Write this lane's row of such an accumulator tile (acc * mul, or zeros) as
+// fp32 to row[0 .. D): 16 bytes per store, the two lanes of a row (hh = 0, 1)
+// filling alternate groups of four columns.  For the split backward's
+// partial gradients, which a combine pass reads once.
+template <int D>
+__device__ __forceinline__ void acc_row_to_f32(float* row, const f32x16 (&acc)[D / 32], float mul,
+                                               bool zero, int hh) {
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = zero ? 0.0f : acc[u][4 * g + e] * mul;
+      *(f32x4*)(row + 32 * u + 8 * g + 4 * hh) = v;
     }
 }
 

@@ -64,6 +64,14 @@ struct BwdArgs {
   int b0 = 0;  // batch index of entry 0 in the dropout counter (packed sequences)
   float* delta;   // workspace: fp32 [B, H, N], D_i = sum_k dO_ik O_ik
   float* lse2;    // workspace: fp32 [B, H, N], LSE_i * log2(e) (+inf for an empty row)
+  // Split backward (16-bit, contiguous, d in {64, 128}): num_splits > 0 splits
+  // dQ's key range and dK/dV's query range that many ways into the fp32
+  // workspaces dqp, dkp, dvp [S][B*H][N][d], then sums them into dq, dk, dv.
+  // 0: every gradient accumulated in one pass.
+  int num_splits = 0;
+  float* dqp = nullptr;
+  float* dkp = nullptr;
+  float* dvp = nullptr;
 };
 
 // Each returns hipSuccess or the launch error.

@@ -207,6 +207,47 @@ def test_split_rejects(lib, kw, expect):
     assert split(lib, **kw) == expect
 
 
+def bsplit(lib, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, splits=2, ws=P, ws_bytes=None,
+           p=0.0, q=P, dq=P):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_split_workspace_size(B, H, N, d, dtype, splits)
+    return lib.fa_bwd_split(q, P, P, P, P, P, dq, P, P, B, H, N, d, dtype, 0.125, 1, None, p, 0,
+                            splits, ws, ws_bytes, None)
+
+
+def test_backward_split_workspace_size():
+    ws = binding.fa_bwd_split_workspace_size
+    base = binding.fa_bwd_workspace_size
+    # fa_bwd's two row arrays, then fp32 partial dQ, dK and dV per split, each
+    # padded to 256 bytes
+    part = ((3 * 2 * 3 * 100 * 64 * 4 + 255) // 256) * 256
+    assert ws(2, 3, 100, 64, 3) == base(2, 3, 100, 64) + 3 * part
+    assert ws(1, 8, 4096, 128, 2) == 2 * 8 * 4096 * 4 + 3 * 2 * 8 * 4096 * 128 * 4
+    assert ws(1, 1, 128, 96, 2) == 0  # MFMA head sizes only
+    assert ws(1, 1, 128, 64, 0) == 0
+    assert ws(1, 1, 128, 64, binding.FA_MAX_SPLITS + 1) == 0
+    assert ws(1, 1, 128, 64, 2, binding.FA_F32) == 0
+    assert ws(1, 1, 1 << 24, 128, 2) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(splits=0), INVALID), (dict(splits=binding.FA_MAX_SPLITS + 1), INVALID),
+    (dict(dtype=binding.FA_F32, ws_bytes=1 << 30), UNSUPPORTED),
+    (dict(d=96, ws_bytes=1 << 30), UNSUPPORTED), (dict(d=256, ws_bytes=1 << 30), UNSUPPORTED),
+    (dict(d=48, ws_bytes=1 << 30), UNSUPPORTED), (dict(N=1 << 24, d=128, ws_bytes=1 << 62), UNSUPPORTED),
+    (dict(ws=None), INVALID), (dict(ws=P + 8), INVALID), (dict(ws_bytes=16), INVALID),
+    (dict(q=None), INVALID), (dict(dq=None), INVALID), (dict(p=1.0), INVALID), (dict(N=0), INVALID),
+    (dict(dtype=7), INVALID),
+])
+def test_backward_split_rejects(lib, kw, expect):
+    assert bsplit(lib, **kw) == expect
+
+
+def test_backward_split_rejects_workspace_one_byte_short(lib):
+    need = lib.fa_bwd_split_workspace_size(2, 3, 100, 128, binding.FA_BF16, 4)
+    assert bsplit(lib, B=2, H=3, N=100, d=128, splits=4, ws_bytes=need - 1) == INVALID
+
+
 def noalloc(lib, ptrs=None, B=1, H=1, N=128, d=64, dtype=binding.FA_BF16, scale=0.125, p=0.0):
     ptrs = ptrs or [P] * 9
     return lib.fa_bwd_noalloc(*ptrs, B, H, N, d, dtype, scale, 0, None, p, 0, None)

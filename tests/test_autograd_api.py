@@ -58,3 +58,19 @@ def test_split_count_per_shape():
     assert split_count(1, 1, 1 << 16, 128, False, 1 << 15) == 64
     # only the MFMA head sizes have a split forward
     assert split_count(1, 1, 4096, 96, True, cus) == 0
+
+
+def test_backward_split_count_per_shape():
+    from io_aware_exact_24_amd.autograd import backward_split_count
+
+    cus = 256
+    # enough units already: the plain backward
+    assert backward_split_count(4, 32, 4096, 128, True, cus) == 0
+    assert backward_split_count(8, 16, 1024, 64, False, cus) == 0
+    # too few units: shares until the units cover the CUs, four tiles each at least
+    assert backward_split_count(1, 8, 4096, 128, True, cus) == 2    # 128 causal pairs
+    assert backward_split_count(1, 1, 4096, 128, True, cus) == 16   # 16 pairs of 66 tiles
+    assert backward_split_count(1, 4, 2048, 64, False, cus) == 4    # 64 blocks of 32 tiles
+    assert backward_split_count(1, 2, 1000, 128, True, cus) == 4    # 8 pairs of 18 tiles
+    assert backward_split_count(1, 2, 300, 64, True, cus) == 0      # 7 tiles: nothing to split
+    assert backward_split_count(1, 1, 4096, 96, True, cus) == 0     # generic kernels: no split

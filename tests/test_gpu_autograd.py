@@ -52,22 +52,30 @@ def test_autograd_matches_oracle(layout, causal, padded):
     assert eo <= TOL_O and max(errs) <= TOL_GRAD
 
 
-def test_small_shapes_take_the_split_forward():
-    # B*H*blocks below the CU count: the forward runs split (as many shares as
-    # split_count picks); results equal fa_fwd_split's with that count bit for
-    # bit and the oracle's within the bar
-    from io_aware_exact_24_amd.autograd import _splits
+def test_small_shapes_take_the_split_passes():
+    # B*H*blocks below the CU count: the forward and the backward run split (as
+    # many shares as split_count / backward_split_count pick); results equal
+    # fa_fwd_split's and fa_bwd_split's with those counts bit for bit and the
+    # oracle's within the bar
+    from io_aware_exact_24_amd.autograd import _bwd_splits, _splits
 
     B, H, N, d = 1, 2, 1000, 128
     inp = draw(B, H, N, d, torch.bfloat16, seed=80)
     q, k, v = (leaf(t, "bhnd") for t in (inp.q, inp.k, inp.v))
+    do = inp.dout.to(DEV)
     s = _splits(q, True)
     assert s >= 2
     o = flash_attention(q, k, v, causal=True)
-    o.backward(inp.dout.to(DEV))
-    o2, _ = binding.forward_split(q.detach(), k.detach(), v.detach(), d ** -0.5, True, None, 0.0, 0, s)
+    sb = _bwd_splits(q, True, (q, k, v, o, do))
+    assert sb >= 2
+    o.backward(do)
+    qd, kd, vd = (t.detach() for t in (q, k, v))
+    o2, lse2 = binding.forward_split(qd, kd, vd, d ** -0.5, True, None, 0.0, 0, s)
+    g2 = binding.backward_split(qd, kd, vd, o2, do, lse2, d ** -0.5, True, None, 0.0, 0, sb)
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), o2)
+    for t, g in zip((q, k, v), g2):
+        assert torch.equal(t.grad, g)
     ro, _ = attention_forward(inp.q, inp.k, inp.v, float(np.float32(d ** -0.5)), True)
     ref = attention_backward(inp.q, inp.k, inp.v, inp.dout, float(np.float32(d ** -0.5)), True)
     assert max_abs(f64(o), ro) <= TOL_O

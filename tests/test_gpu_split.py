@@ -1,14 +1,16 @@
-"""GPU: the split-KV forward (fa_fwd_split) against the fp64 oracle and
-against fa_fwd on the same inputs."""
+"""GPU: the split-KV forward (fa_fwd_split) and the split backward
+(fa_bwd_split) against the fp64 oracle and against fa_fwd / fa_bwd on the same
+inputs."""
 
 import numpy as np
 import pytest
 import torch
 
-from fa_testlib import TOL_LSE, TOL_O, f64, gpu_forward, key_lens_list, max_abs, note
+from fa_testlib import (TOL_GRAD, TOL_LSE, TOL_O, f64, gpu_backward, gpu_forward, key_lens_list,
+                        max_abs, note, rel_l2)
 from io_aware_exact_24_amd import binding
 from io_aware_exact_24_amd.workloads import Inputs, draw
-from oracle import attention_forward
+from oracle import attention_backward, attention_forward
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -54,3 +56,89 @@ def test_split_forward(case):
     assert eo <= TOL_O and el <= TOL_LSE
     assert np.array_equal(np.isneginf(f64(lse)), np.isneginf(rlse))
     assert d1 <= TOL_O
+
+
+def worst_column(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    a, b = a.reshape(-1, a.shape[-1]), b.reshape(-1, b.shape[-1])
+    return max(rel_l2(a[:, c], b[:, c]) for c in range(a.shape[1]))
+
+
+def _inputs(B, H, N, d, dt, lens, seed):
+    inp = draw(B, H, N, d, dt, seed=seed, padded=lens == "draw")
+    if isinstance(lens, list):
+        inp = Inputs(inp.q, inp.k, inp.v, inp.dout, torch.tensor(lens, dtype=torch.int32))
+    return inp
+
+
+BWD_CASES = [
+    # B, H, N, d, dtype, causal, key lengths, dropout p, splits
+    (1, 2, 1000, 128, torch.bfloat16, True, None, 0.0, 3),
+    (2, 1, 513, 64, torch.bfloat16, False, "draw", 0.1, 4),
+    (1, 2, 300, 128, torch.float16, True, None, 0.1, 2),   # 3 key blocks: a pair of one block
+    (1, 1, 100, 64, torch.bfloat16, False, None, 0.0, 5),  # more shares than tiles
+    (2, 2, 700, 128, torch.bfloat16, True, [0, 650], 0.0, 7),  # an empty batch entry
+    (1, 3, 2048, 64, torch.bfloat16, True, None, 0.2, 16),
+    (1, 1, 4096, 128, torch.bfloat16, True, None, 0.0, 8),
+    (1, 2, 1536, 64, torch.float16, False, "draw", 0.0, 3),
+]
+
+
+def _bwd_id(c):
+    B, H, N, d, dt, causal, lens, p, S = c
+    return "B{}H{}N{}d{}-{}{}{}{}-S{}".format(B, H, N, d, "bf16" if dt == torch.bfloat16 else "fp16",
+                                             "-causal" if causal else "", "-pad" if lens else "",
+                                             f"-p{p}" if p else "", S)
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=_bwd_id)
+def test_split_backward(case):
+    B, H, N, d, dt, causal, lens, p, S = case
+    inp = _inputs(B, H, N, d, dt, lens, BWD_CASES.index(case) + 900)
+    scale, seed = float(np.float32(1 / np.sqrt(d))), 0x0123456789ABCDEF
+    note(f"split backward {_bwd_id(case)}")
+    q, k, v, do = (t.to(DEV) for t in (inp.q, inp.k, inp.v, inp.dout))
+    kl = None if inp.key_lens is None else inp.key_lens.to(DEV)
+    o, lse = binding.forward(q, k, v, scale, causal, kl, p, seed)
+    g = binding.backward_split(q, k, v, o, do, lse, scale, causal, kl, p, seed, S)
+    g2 = binding.backward_split(q, k, v, o, do, lse, scale, causal, kl, p, seed, S)
+    torch.cuda.synchronize()
+    g1 = gpu_backward(inp, o, lse, scale, causal, p, seed)
+    ref = attention_backward(inp.q, inp.k, inp.v, inp.dout, scale, causal, key_lens_list(inp), p,
+                             seed)
+    errs = [rel_l2(f64(a), r) for a, r in zip(g, ref)]
+    cols = [worst_column(f64(a), r) for a, r in zip(g, ref)]
+    vs1 = [rel_l2(f64(a), f64(b)) for a, b in zip(g, g1)]
+    note(f"  vs oracle relL2 dQ={errs[0]:.2e} dK={errs[1]:.2e} dV={errs[2]:.2e} worst column "
+         f"{max(cols):.2e}; vs fa_bwd {max(vs1):.2e}")
+    assert max(errs) <= TOL_GRAD and max(cols) <= 2 * TOL_GRAD
+    assert max(vs1) <= TOL_GRAD
+    for a, b in zip(g, g2):  # deterministic
+        assert torch.equal(a, b)
+    if isinstance(lens, list):  # keys of an empty batch entry: zero gradients
+        for b, n in enumerate(lens):
+            if n == 0:
+                assert not g[1][b].any() and not g[2][b].any()
+
+
+@pytest.mark.parametrize("dt,d,causal,lens,p", [
+    (torch.bfloat16, 128, True, None, 0.0),
+    (torch.bfloat16, 64, False, "draw", 0.1),
+    (torch.float16, 128, False, None, 0.2),
+    (torch.float16, 64, True, "draw", 0.0),
+], ids=lambda x: str(x).replace("torch.", ""))
+def test_split_backward_one_share_equals_fa_bwd(dt, d, causal, lens, p):
+    # One share: the same tiles in the same order, the fp32 partial converted
+    # once, so every bit equals fa_bwd's.
+    B, H, N = 2, 3, 333
+    inp = _inputs(B, H, N, d, dt, lens, 77 + d)
+    scale, seed = float(np.float32(1 / np.sqrt(d))), 0x5EED
+    note(f"split backward S=1 {dt} d={d} causal={causal} lens={lens} p={p}")
+    q, k, v, do = (t.to(DEV) for t in (inp.q, inp.k, inp.v, inp.dout))
+    kl = None if inp.key_lens is None else inp.key_lens.to(DEV)
+    o, lse = binding.forward(q, k, v, scale, causal, kl, p, seed)
+    g = binding.backward_split(q, k, v, o, do, lse, scale, causal, kl, p, seed, 1)
+    torch.cuda.synchronize()
+    g1 = gpu_backward(inp, o, lse, scale, causal, p, seed)
+    for name, a, b in zip(("dq", "dk", "dv"), g, g1):
+        assert torch.equal(a, b), name
