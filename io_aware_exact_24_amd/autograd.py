@@ -43,13 +43,16 @@ def split_count(B, H, N, d, causal, cus):
     """Key splits for the forward of one shape (0: the plain fa_fwd).
 
     The plain forward launches one workgroup per 128-query block (causal ones
-    in pairs, so each has the same work).  When that leaves CUs idle, the
-    split forward (one workgroup per query block and key share) gets enough
-    shares for one workgroup per CU, at least 2, capped so that every share
-    keeps at least four 64-key tiles of the longest block and at
-    FA_MAX_SPLITS.  (Measured on small shapes: more shares than that lose
-    more to the combine pass and the shorter shares than they gain.)  Only
-    the MFMA head sizes have a split forward.
+    in pairs, so each has the same work), two per CU.  When that leaves CUs
+    idle, the split forward (one workgroup per query block and key share)
+    takes as many shares as fit one workgroup per CU, two with a causal mask
+    (its blocks have unequal work, which more shares even out), at least 2;
+    each share keeps at least eight 64-key tiles of the longest block, and
+    there are at most FA_MAX_SPLITS.  Short sequences (under 32 key tiles)
+    are split only when the plain grid is tiny (16 workgroups or fewer):
+    otherwise the combine pass costs more than the shorter shares save.
+    Only the MFMA head sizes have a split forward.  (Rules fitted to
+    back-to-back timings of both passes over 16 shapes.)
     """
     if d not in (64, 128):
         return 0
@@ -57,8 +60,11 @@ def split_count(B, H, N, d, causal, cus):
     plain = B * H * ((blocks + 1) // 2 if causal else blocks)
     if plain >= cus:
         return 0
-    want = max(2, -(-cus // (B * H * blocks)))  # ceil
-    cap = min(max(((N + 63) // 64) // 4, 1), binding.FA_MAX_SPLITS)
+    tiles = (N + 63) // 64
+    if tiles < 32 and plain > 16:
+        return 0
+    want = max(2, (2 if causal else 1) * cus // (B * H * blocks))
+    cap = min(max(tiles // 8, 1), binding.FA_MAX_SPLITS)
     s = min(want, cap)
     return s if s >= 2 else 0
 
@@ -69,10 +75,12 @@ def backward_split_count(B, H, N, d, causal, cus):
     The dK/dV stage runs one persistent workgroup per CU over work units of
     one 128-key block (with a causal mask, a pair of blocks of equal total
     work).  When there are fewer units than CUs, fa_bwd_split cuts each
-    unit's query tiles (and each query block's key tiles for dQ) into enough
-    shares for one unit per CU, at least 2, capped so that every share keeps
-    at least four 64-row tiles and at FA_MAX_SPLITS.  Only the MFMA head sizes
-    have a split backward.
+    unit's query tiles (and each query block's key tiles for dQ) into as many
+    shares as keep one unit per CU, at least 2, each with at least four
+    64-row tiles, at most FA_MAX_SPLITS.  With half the CUs or more already
+    busy, two shares pay only for long units (64 tiles or more).  Only the
+    MFMA head sizes have a split backward.  (Rules fitted to back-to-back
+    timings of both passes over 16 shapes.)
     """
     if d not in (64, 128):
         return 0
@@ -82,7 +90,9 @@ def backward_split_count(B, H, N, d, causal, cus):
         return 0
     tiles = (N + 63) // 64
     per_unit = tiles + 2 if causal else tiles  # a causal pair's tiles, both blocks
-    want = max(2, -(-cus // units))
+    if 2 * units >= cus and per_unit < 64:
+        return 0
+    want = max(2, cus // units)
     cap = min(max(per_unit // 4, 1), binding.FA_MAX_SPLITS)
     s = min(want, cap)
     return s if s >= 2 else 0

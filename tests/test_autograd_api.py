@@ -48,12 +48,15 @@ def test_split_count_per_shape():
     # shapes that fill the GPU with the plain forward take no split
     assert split_count(4, 32, 4096, 128, True, cus) == 0
     assert split_count(8, 16, 1024, 64, False, cus) == 0
-    # few query blocks: enough shares for one workgroup per CU, at least 2 ...
-    assert split_count(1, 1, 4096, 128, True, cus) == 8    # 32 blocks x 8 = 256
+    # few query blocks: shares for one workgroup per CU (causal: two), at least 2 ...
+    assert split_count(1, 1, 4096, 128, True, cus) == 8    # 64 tiles: 8 shares of 8
     assert split_count(1, 8, 2048, 64, False, cus) == 2    # 128 blocks x 2 = 256
-    assert split_count(1, 4, 8192, 128, True, cus) == 2    # 128 causal pairs: at least 2
-    # ... but at least four 64-key tiles per share, and at most FA_MAX_SPLITS
-    assert split_count(1, 2, 1000, 128, True, cus) == 4    # 16 tiles -> 4 shares
+    assert split_count(1, 4, 8192, 128, True, cus) == 2    # 256 blocks x 2 = 512 = 2 per CU
+    assert split_count(1, 2, 8192, 64, True, cus) == 4     # 128 blocks x 4 = 512
+    # ... but at least eight 64-key tiles per share, and at most FA_MAX_SPLITS
+    assert split_count(1, 2, 1000, 128, True, cus) == 2    # 16 tiles -> 2 shares of 8
+    assert split_count(2, 4, 1024, 128, False, cus) == 0   # 16 tiles, 64 workgroups
+    assert split_count(1, 3, 4096, 64, False, cus) == 2    # 96 blocks: 2 shares fill the CUs
     assert split_count(1, 1, 128, 64, False, cus) == 0     # 2 tiles: nothing to split
     assert split_count(1, 1, 1 << 16, 128, False, 1 << 15) == 64
     # only the MFMA head sizes have a split forward
@@ -74,3 +77,6 @@ def test_backward_split_count_per_shape():
     assert backward_split_count(1, 2, 1000, 128, True, cus) == 4    # 8 pairs of 18 tiles
     assert backward_split_count(1, 2, 300, 64, True, cus) == 0      # 7 tiles: nothing to split
     assert backward_split_count(1, 1, 4096, 96, True, cus) == 0     # generic kernels: no split
+    # half the CUs busy: two shares only for long units
+    assert backward_split_count(2, 8, 2048, 128, True, cus) == 0    # 128 pairs of 34 tiles
+    assert backward_split_count(1, 16, 1024, 64, False, cus) == 0   # 128 blocks of 16 tiles
