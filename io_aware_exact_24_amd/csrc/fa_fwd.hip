@@ -73,8 +73,18 @@ struct FwdCfg {
   static_assert(LOADS * THREADS == BN * CHUNKS, "tile/thread mismatch");
 };
 
+// Waves per SIMD: two, or three at d = 64 without a causal mask or dropout,
+// whose registers then fit 168 per lane without spills (LDS: 32 KB per
+// workgroup).  The d = 64 loop has half the MFMA work of d = 128 per score
+// but the same exponentials, sums and maxima, so a third wave to overlap
+// them pays.
+template <int D, bool CAUSAL, bool DROPOUT>
+constexpr int fwd_waves() { return D == 64 && !CAUSAL && !DROPOUT ? 3 : 2; }
+
 template <typename E, int D, bool CAUSAL, bool DROPOUT, bool SPLIT, bool CONTIG>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(fwd_waves<D, CAUSAL, DROPOUT>(),
+                                              fwd_waves<D, CAUSAL, DROPOUT>())))
 void fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
   using V8 = typename Elem<E>::v8;
