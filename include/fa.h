@@ -131,9 +131,8 @@ typedef struct {
  *     dropout combination.
  *   FA_BF16, FA_F16 at d in {32, 96, 256}, and FA_F32 at every d in
  *     {32, 64, 96, 128, 256}: generic kernels (fp32 arithmetic on the vector
- *     ALUs, 32-row tiles in LDS; correct, not tuned).  FA_F32 takes no
- *     dropout (FA_ERR_UNSUPPORTED); its forward at d in {64, 128} is a
- *     one-thread-per-query kernel meant for the small single-head workload.
+ *     ALUs, 32-row tiles in LDS, eight threads per row).  FA_F32 takes no
+ *     dropout (FA_ERR_UNSUPPORTED).
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, fa_dtype dtype, float scale, int causal,

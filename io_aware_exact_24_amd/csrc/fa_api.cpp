@@ -160,8 +160,6 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   hipError_t e;
   if (mfma_path(dtype, d))
     e = fa::launch_fwd_16(a, stream);
-  else if (dtype == FA_F32 && (d == 64 || d == 128))
-    e = fa::launch_fwd_f32(a, stream);
   else
     e = fa::launch_fwd_generic(a, (int)dtype, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

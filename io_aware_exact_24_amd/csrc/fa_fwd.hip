@@ -47,7 +47,6 @@ struct FwdParams {
   Strides sq, sk, sv, so;  // element strides (batch, head, row); d is contiguous
   int H, N, num_qblocks;
   int b0;  // added to the batch index in the dropout counter
-  int causal;  // fp32 kernel only (the 16-bit kernel takes it as a template argument)
   float scale_log2;  // scale * log2(e): scores enter exp2 in these units
   uint32_t drop_threshold;
   float drop_scale;
@@ -500,77 +499,6 @@ void fwd_kernel(FwdParams p) {
   }  // item
 }
 
-// fp32 path: one thread per query row, K/V tiles of 64 keys staged in LDS and
-// read as broadcasts; online softmax over each tile in fp32 registers.
-template <int D>
-__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
-  constexpr int BN = 64;
-  __shared__ float ks[BN][D];
-  __shared__ float vs[BN][D];
-  const int N = p.N;
-  const int nqb = (N + 63) / 64;
-  const int head = blockIdx.x / nqb;
-  const int qb = blockIdx.x - head * nqb;
-  const int bi = head / p.H, hi = head - bi * p.H;
-  const int qi = qb * 64 + threadIdx.x;
-  const int causal = p.causal;
-  int L = N;
-  if (p.key_lens) L = min(max(p.key_lens[bi], 0), N);
-  const int kend = causal ? min(L, qb * 64 + 64) : L;
-  const float* qg = (const float*)p.q + (bi * p.sq.b + hi * p.sq.h);
-  const float* kg = (const float*)p.k + (bi * p.sk.b + hi * p.sk.h);
-  const float* vg = (const float*)p.v + (bi * p.sv.b + hi * p.sv.h);
-  float* og = (float*)p.o + (bi * p.so.b + hi * p.so.h);
-  const float scale_log2 = p.scale_log2;
-
-  float qr[D], acc[D];
-#pragma unroll
-  for (int c = 0; c < D; ++c) {
-    qr[c] = qi < N ? qg[(int64_t)qi * p.sq.n + c] : 0.0f;
-    acc[c] = 0.0f;
-  }
-  float m = -INFINITY, l = 0.0f;
-  for (int kb = 0; kb < kend; kb += BN) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < BN * D; idx += 64) {
-      const int row = kb + idx / D;
-      ks[idx / D][idx % D] = row < N ? kg[(int64_t)row * p.sk.n + idx % D] : 0.0f;
-      vs[idx / D][idx % D] = row < N ? vg[(int64_t)row * p.sv.n + idx % D] : 0.0f;
-    }
-    __syncthreads();
-    float s[BN];
-    float mx = -INFINITY;
-    for (int j = 0; j < BN; ++j) {
-      float dot = 0.0f;
-#pragma unroll
-      for (int c = 0; c < D; ++c) dot = fmaf(qr[c], ks[j][c], dot);
-      const int key = kb + j;
-      const bool ok = key < L && (!causal || key <= qi);
-      s[j] = ok ? dot : -INFINITY;
-      mx = fmaxf(mx, s[j]);
-    }
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = exp2f((m - m_use) * scale_log2);
-    m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int c = 0; c < D; ++c) acc[c] *= alpha;
-    for (int j = 0; j < BN; ++j) {
-      const float e = exp2f((s[j] - m_use) * scale_log2);
-      l += e;
-#pragma unroll
-      for (int c = 0; c < D; ++c) acc[c] = fmaf(e, vs[j][c], acc[c]);
-    }
-  }
-  if (qi < N) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-#pragma unroll
-    for (int c = 0; c < D; ++c) og[(int64_t)qi * p.so.n + c] = acc[c] * inv;
-    p.lse[(size_t)head * N + qi] = l > 0.0f ? (m * scale_log2 + log2f(l)) * kLn2 : -INFINITY;
-  }
-}
-
 // Split-KV combine: O_i = sum_s w_s O_i^(s) / sum_s w_s with w_s = exp(LSE_i^(s) - m_i),
 // m_i = max_s LSE_i^(s), and LSE_i = m_i + ln sum_s w_s (each split's O is
 // normalised by its own row sum l_s, and exp(LSE^(s)) = l_s e^(m_s)).  Eight
@@ -684,7 +612,6 @@ FwdParams make_params(const FwdArgs& a) {
   p.N = a.N;
   p.b0 = a.b0;
   p.num_qblocks = 0;
-  p.causal = a.causal != 0;
   p.scale_log2 = a.scale * kLog2e;
   p.drop_threshold = a.drop_threshold;
   p.drop_scale = a.drop_scale;
@@ -702,16 +629,6 @@ FwdParams make_params(const FwdArgs& a) {
 hipError_t launch_fwd_16(const FwdArgs& a, hipStream_t s) {
   FwdParams p = make_params(a);
   return a.fp16 ? dispatch_d<f16>(p, a, s) : dispatch_d<bf16>(p, a, s);
-}
-
-hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
-  FwdParams p = make_params(a);
-  const int grid = a.B * a.H * ((a.N + 63) / 64);
-  if (a.d == 64)
-    hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3(grid), dim3(64), 0, s, p);
-  else
-    hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3(grid), dim3(64), 0, s, p);
-  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -76,7 +76,6 @@ struct BwdArgs {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_16(const FwdArgs& a, hipStream_t s);  // bf16 or fp16
-hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 // Backward stages, selected by a bit mask and launched in this order: the
 // per-row preprocessing alone (D and LSE*log2e into the workspace), the dQ
 // kernel (which also computes those per-row terms and writes them to the
