@@ -129,7 +129,11 @@ typedef struct {
  * Head sizes and kernels:
  *   FA_BF16, FA_F16 at d in {64, 128}: the MFMA kernels, every mask and
  *     dropout combination.
- *   FA_BF16, FA_F16 at d in {32, 96, 256}, and FA_F32 at every d in
+ *   FA_BF16, FA_F16 at d in {32, 96}: the same MFMA kernels of width 64 and
+ *     128, the head dimension zero-padded on chip (columns past d are read
+ *     as zeros and never written), when every tensor's (b, h) slice, N + 256
+ *     rows of its row stride, spans fewer than 2^31 bytes; else as below.
+ *   FA_BF16, FA_F16 at d = 256, and FA_F32 at every d in
  *     {32, 64, 96, 128, 256}: generic kernels (fp32 arithmetic on the vector
  *     ALUs, 32-row tiles in LDS, eight threads per row).  FA_F32 takes no
  *     dropout (FA_ERR_UNSUPPORTED).

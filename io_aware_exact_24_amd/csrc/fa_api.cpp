@@ -29,10 +29,23 @@ int64_t elems(int B, int H, int N, int d) {
 
 bool valid_dtype(fa_dtype t) { return t == FA_F32 || t == FA_BF16 || t == FA_F16; }
 bool is16(fa_dtype t) { return t == FA_BF16 || t == FA_F16; }
-// The MFMA kernels: 16-bit types at d = 64 and 128.  Every other supported
-// combination runs on the generic kernels.
+// The MFMA kernels: 16-bit types at d = 64 and 128 (the split entry points
+// take only these).  Every other supported combination runs on the generic
+// kernels, except padded_path below.
 bool mfma_path(fa_dtype t, int d) { return is16(t) && (d == 64 || d == 128); }
 uint64_t elem_bytes(fa_dtype t) { return t == FA_F32 ? 4 : 2; }
+
+// 16-bit d = 32 and 96 run on the MFMA kernels of width 64 and 128 with the
+// columns past d zero-padded on chip.  Those kernels park the lanes of the
+// padding columns at byte offset 2^31 of a slice, so every tensor's (b, h)
+// slice ((N + 256) rows of its row stride) must span fewer bytes than that;
+// otherwise the generic kernels run.
+bool padded_path(fa_dtype t, int d, int N, std::initializer_list<int64_t> row_strides) {
+  if (!is16(t) || (d != 32 && d != 96)) return false;
+  for (int64_t r : row_strides)
+    if (((uint64_t)N + 256) * (uint64_t)r * 2 >= (1ull << 31)) return false;
+  return true;
+}
 
 // The kernels address one (b, h) slice of a tensor through a buffer resource
 // whose byte range, and every tile offset inside it (rows up to 256 past the
@@ -158,7 +171,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     a.lsepart = (float*)((char*)workspace + pad256((size_t)num_splits * rows * d * 4));
   }
   hipError_t e;
-  if (mfma_path(dtype, d))
+  if (mfma_path(dtype, d) || padded_path(dtype, d, N, {a.sq.n, a.sk.n, a.sv.n, a.so.n}))
     e = fa::launch_fwd_16(a, stream);
   else
     e = fa::launch_fwd_generic(a, (int)dtype, stream);
@@ -287,8 +300,11 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.dvp = dvp;
   fa::Strides* dst[8] = {&a.sq, &a.sk, &a.sv, &a.so, &a.sdo, &a.sdq, &a.sdk, &a.sdv};
   for (int t = 0; t < 8; ++t) *dst[t] = to_strides(strides ? &strides[t] : nullptr, H, N, d);
-  const hipError_t e = mfma_path(dtype, d) ? fa::launch_bwd_16(a, stages, stream)
-                                           : fa::launch_bwd_generic(a, (int)dtype, stages, stream);
+  const bool mfma = mfma_path(dtype, d) ||
+                    padded_path(dtype, d, N, {a.sq.n, a.sk.n, a.sv.n, a.so.n, a.sdo.n, a.sdq.n, a.sdk.n,
+                                              a.sdv.n});
+  const hipError_t e = mfma ? fa::launch_bwd_16(a, stages, stream)
+                            : fa::launch_bwd_generic(a, (int)dtype, stages, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -29,6 +29,7 @@ hipError_t launch_bwd_16(const BwdArgs& a, int stages, hipStream_t s) {
   p.key_lens = a.key_lens;
   p.H = a.H;
   p.N = a.N;
+  p.dl = a.d;
   p.b0 = a.b0;
   p.num_blocks = 0;
   p.units = 0;
@@ -46,23 +47,25 @@ hipError_t launch_bwd_16(const BwdArgs& a, int stages, hipStream_t s) {
   const int heads = a.B * a.H;
   const bool dropout = a.dropout_p > 0.0f;
   const bool causal = a.causal != 0;
-  const int64_t d = a.d;
+  // Head sizes 32 and 96 run on the kernels of width 64 and 128.
+  const int width = a.d <= 64 ? 64 : 128;
+  const int64_t d = width;
   const bool contig = p.sq.n == d && p.sk.n == d && p.sv.n == d && p.so.n == d && p.sdo.n == d &&
                       p.sdq.n == d && p.sdk.n == d && p.sdv.n == d;
   if (stages & kBwdPre) {
-    const hipError_t e = launch_bwd_pre(p, a.fp16, a.d, (int64_t)heads * a.N, s);
+    const hipError_t e = launch_bwd_pre(p, a.fp16, width, (int64_t)heads * a.N, s);
     if (e != hipSuccess) return e;
   }
   if (stages & kBwdQ) {
-    const hipError_t e = launch_bwd_dq(p, a.fp16, a.d, causal, dropout, contig, heads, s);
+    const hipError_t e = launch_bwd_dq(p, a.fp16, width, causal, dropout, contig, heads, s);
     if (e != hipSuccess) return e;
   }
   if (stages & kBwdKV) {
-    const hipError_t e = launch_bwd_dkdv(p, a.fp16, a.d, causal, dropout, contig, heads, s);
+    const hipError_t e = launch_bwd_dkdv(p, a.fp16, width, causal, dropout, contig, heads, s);
     if (e != hipSuccess) return e;
   }
   if (a.num_splits > 0 && (stages & (kBwdQ | kBwdKV)))
-    return launch_bwd_combine(p, a.fp16, a.d, (int64_t)heads * a.N, s);
+    return launch_bwd_combine(p, a.fp16, width, (int64_t)heads * a.N, s);
   return hipSuccess;
 }
 

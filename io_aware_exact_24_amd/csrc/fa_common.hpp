@@ -312,23 +312,33 @@ __device__ __forceinline__ void acc_row_to_f32(float* row, const f32x16 (&acc)[D
     }
 }
 
+// Per-lane buffer offset that no access can reach: a lane whose 16-byte chunk
+// lies past a tensor's head size (the kernels of width D run head sizes
+// dl < D with the columns [dl, D) zero-padded on chip) starts from it, so its
+// loads read zeros and its stores are dropped by the buffer range check.
+// Valid offsets stay below 2^31 (the host routes a tensor here only when its
+// slice spans fewer bytes), so poison plus any tile offset neither wraps nor
+// falls in range.
+constexpr uint32_t kPoison = 0x80000000u;
+
 // Copy rows [0, min(nrows, 32)) of such an LDS tile to the rows of a tensor
 // slice starting at dst, rows `sn` elements apart, 16 bytes per lane: every
 // store instruction writes 64 / (D/8) whole rows.  The stores go through a
 // buffer resource whose byte range ends with row min(nrows, 32) - 1, so the
 // range check drops the rows past it (no branch; one 32-bit per-lane offset
 // plus a uniform step per row: callers keep each slice's byte span within
-// 32 bits).
+// 32 bits).  Columns [dl, D) are not written.
 template <int D, typename E>
 __device__ __forceinline__ void lds_rows_to_buffer(const E* tile, E* dst, int64_t sn, int nrows,
-                                                   int lane) {
+                                                   int lane, int dl) {
   constexpr int CH = D / 8, RPI = 64 / CH, ES = (int)sizeof(E);
   typedef E v8 __attribute__((ext_vector_type(8)));
   asm volatile("" : "+v"(lane));  // see acc_rows_to_lds
   const int c = lane % CH;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, rows_bytes(min(nrows, 32), sn, D, ES));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, rows_bytes(min(nrows, 32), sn, dl, ES));
   const uint32_t rb = (uint32_t)sn * ES;
-  const uint32_t off0 = (uint32_t)(lane / CH) * rb + (uint32_t)(c * 8 * ES);
+  const uint32_t off0 =
+      c * 8 < dl ? (uint32_t)(lane / CH) * rb + (uint32_t)(c * 8 * ES) : kPoison;
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CH;

@@ -46,6 +46,7 @@ struct FwdParams {
   const int32_t* key_lens;
   Strides sq, sk, sv, so;  // element strides (batch, head, row); d is contiguous
   int H, N, num_qblocks;
+  int dl;  // head size of the tensors, <= D: columns [dl, D) read as zero and are not written
   int b0;  // added to the batch index in the dropout counter
   float scale_log2;  // scale * log2(e): scores enter exp2 in these units
   uint32_t drop_threshold;
@@ -158,14 +159,14 @@ void fwd_kernel(FwdParams p) {
   // The copies cover the tiles [0, nkb) only: copies past them (issued without
   // a branch) read zeros without touching memory.
   const int krows = min((jt0 + nkb) * BN, N);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, rows_bytes(krows, skn, D, ES));
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, rows_bytes(krows, svn, D, ES));
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, rows_bytes(krows, skn, p.dl, ES));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, rows_bytes(krows, svn, p.dl, ES));
 
   // Q^T as the B operand of S^T = K Q^T: lane holds Q[qi][16c + 8hh .. +7].
   V8 qreg[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    if (qi < N) {
+    if (qi < N && 16 * c + 8 * hh < p.dl) {
       qreg[c] = *(const V8*)(qg + (int64_t)qi * sqn + 16 * c + 8 * hh);
     } else {
 #pragma unroll
@@ -183,9 +184,9 @@ void fwd_kernel(FwdParams p) {
   uint32_t kld0, vld0;
   {
     const int r = wave * 64 / C::CHUNKS + lane / C::CHUNKS, pc = lane % C::CHUNKS;
-    const int lch = (pc ^ swz<D>(r)) * 8;
-    kld0 = (uint32_t)(r * skn + lch) * ES;
-    vld0 = (uint32_t)(r * svn + lch) * ES;
+    const int lch = (pc ^ swz<D>(r)) * 8;  // first column of the chunk this lane copies
+    kld0 = lch < p.dl ? (uint32_t)(r * skn + lch) * ES : kPoison;
+    vld0 = lch < p.dl ? (uint32_t)(r * svn + lch) * ES : kPoison;
   }
   // Row strides in bytes, and the byte step between copy rounds.
   const uint32_t krb = (uint32_t)skn * ES, vrb = (uint32_t)svn * ES;
@@ -492,7 +493,7 @@ void fwd_kernel(FwdParams p) {
     {
       E* ot = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
       acc_rows_to_lds<D, E>(ot, oacc, inv, false, li, hh);
-      lds_rows_to_buffer<D, E>(ot, og + (int64_t)qw * son, son, N - qw, lane);
+      lds_rows_to_buffer<D, E>(ot, og + (int64_t)qw * son, son, N - qw, lane, p.dl);
     }
     if (qi < N && hh == 0) p.lse[(size_t)head * N + qi] = lse_out;
   }
@@ -588,7 +589,8 @@ hipError_t dispatch_d(FwdParams& p, const FwdArgs& a, hipStream_t s) {
   const int heads = a.B * a.H;
   const bool split = a.num_splits > 0;
   const bool causal = a.causal != 0;
-  if (a.d == 64) {
+  // Head sizes 32 and 96 run on the kernels of width 64 and 128.
+  if (a.d <= 64) {
     p.num_qblocks = (a.N + FwdCfg<64>::BM - 1) / FwdCfg<64>::BM;
     return dispatch_s<E, 64>(p, heads, split, causal, dropout, s);
   }
@@ -610,6 +612,7 @@ FwdParams make_params(const FwdArgs& a) {
   p.so = a.so;
   p.H = a.H;
   p.N = a.N;
+  p.dl = a.d;
   p.b0 = a.b0;
   p.num_qblocks = 0;
   p.scale_log2 = a.scale * kLog2e;

@@ -1,5 +1,7 @@
-"""GPU parity of the generic kernels: head sizes 32, 96 and 256 in every type,
-and the fp32 backward (also at 64 and 128), against the fp64 oracle.
+"""GPU parity of head sizes 32, 96 and 256 in every type, and of the fp32
+backward (also at 64 and 128), against the fp64 oracle.  16-bit d = 32 and 96
+run on the MFMA kernels of width 64 and 128 with the head dimension
+zero-padded on chip; d = 256 and every fp32 case run on the generic kernels.
 
 Tolerances: 16-bit types as everywhere (O max |err| <= 2e-2, LSE <= 1e-3,
 gradients whole-tensor relative L2 <= 2e-2 and worst head-dimension column
