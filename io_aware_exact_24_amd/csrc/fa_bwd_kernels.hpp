@@ -209,6 +209,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   };
 
   const int N = p.N;
+  // Head size of the tensors: columns [dl, D) are zero-padded on chip.  The
+  // kernels with compile-time strides run only at dl = D.
+  const int dl = CONTIG ? D : p.dl;
   const int nb = p.num_blocks;
   // Work units: with a causal mask key block b sees nit - 2b query tiles, so a
   // unit is the pair of blocks w and nb-1-w (every unit the same work);
@@ -322,7 +325,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       const V4 z = {(E)0.0f, (E)0.0f, (E)0.0f, (E)0.0f};
 #pragma unroll
       for (int c = 0; c < D / 4; c += 2) {
-        if (4 * c + 4 * hh < p.dl) {
+        if (4 * c + 4 * hh < dl) {
           *(V4*)(dkg + (int64_t)key * (CONTIG ? D : p.sdk.n) + 4 * c + 4 * hh) = z;
           *(V4*)(dvg + (int64_t)key * (CONTIG ? D : p.sdv.n) + 4 * c + 4 * hh) = z;
         }
@@ -341,8 +344,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int sqn = CONTIG ? D : (int)p.sq.n, son_ = CONTIG ? D : (int)p.sdo.n;
   const int skn = CONTIG ? D : (int)p.sk.n, svn = CONTIG ? D : (int)p.sv.n;
   const int sdkn = CONTIG ? D : (int)p.sdk.n, sdvn = CONTIG ? D : (int)p.sdv.n;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qg, rows_bytes(N, sqn, p.dl, ES));
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(dog, rows_bytes(N, son_, p.dl, ES));
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qg, rows_bytes(N, sqn, dl, ES));
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(dog, rows_bytes(N, son_, dl, ES));
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lse2 + (size_t)head * N, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.delta + (size_t)head * N, (uint32_t)N * 4);
   // Copy i of this lane fills chunk slot (i * NW + wave) * 64 + lane: row
@@ -358,8 +361,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   {
     const int r = wrow + lane / C::CHUNKS, pc = lane % C::CHUNKS;
     const int lch = (pc ^ swz<D>(r)) * 8;  // first column of the chunk this lane copies
-    ldl_q = lch < p.dl ? (uint32_t)((lane / C::CHUNKS) * sqn + lch) * ES : kPoison;
-    ldl_o = lch < p.dl ? (uint32_t)((lane / C::CHUNKS) * son_ + lch) * ES : kPoison;
+    ldl_q = lch < dl ? (uint32_t)((lane / C::CHUNKS) * sqn + lch) * ES : kPoison;
+    ldl_o = lch < dl ? (uint32_t)((lane / C::CHUNKS) * son_ + lch) * ES : kPoison;
   }
   // K rows of block (head at hoff, first key kb_) straight into registers
   // (this lane's key, rows past N read as zero), V rows into skv with the
@@ -368,19 +371,19 @@ void bwd_dkdv_kernel(BwdParams p) {
   auto fetch_kv = [&](int head_, int kb_, V8 (&kdst)[KC]) __attribute__((always_inline)) {
     const int b_ = head_ / p.H, h_ = head_ - b_ * p.H;
     const __amdgpu_buffer_rsrc_t krs =
-        make_rsrc((const E*)p.k + (b_ * p.sk.b + h_ * p.sk.h), rows_bytes(N, skn, p.dl, ES));
+        make_rsrc((const E*)p.k + (b_ * p.sk.b + h_ * p.sk.h), rows_bytes(N, skn, dl, ES));
     const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc((const E*)p.v + (b_ * p.sv.b + h_ * p.sv.h), rows_bytes(N, svn, p.dl, ES));
+        make_rsrc((const E*)p.v + (b_ * p.sv.b + h_ * p.sv.h), rows_bytes(N, svn, dl, ES));
     const uint32_t krow = (uint32_t)(min(kb_ + 32 * wave + li, N) * skn) * ES + (uint32_t)(16 * hh);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       kdst[c] = __builtin_bit_cast(
-          V8, __builtin_amdgcn_raw_buffer_load_b128(krs, 16 * c + 8 * hh < p.dl ? krow + 32 * c : kPoison, 0, 0));
+          V8, __builtin_amdgcn_raw_buffer_load_b128(krs, 16 * c + 8 * hh < dl ? krow + 32 * c : kPoison, 0, 0));
     const int r = wrow + lane / C::CHUNKS, pc = lane % C::CHUNKS;
     const int vch = (pc ^ swz<D>(r)) * 8;
     const uint32_t vrb = (uint32_t)svn * ES;
     const uint32_t vbase = tile_offset<CONTIG>(
-        vch < p.dl ? (uint32_t)((lane / C::CHUNKS) * svn + vch) * ES : kPoison, kb_ + wrow, vrb);
+        vch < dl ? (uint32_t)((lane / C::CHUNKS) * svn + vch) * ES : kPoison, kb_ + wrow, vrb);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -707,8 +710,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     acc_rows_to_lds<D, E>(kt, dkacc, p.scale, zero, li, hh);
     acc_rows_to_lds<D, E>(vt, dvacc, 1.0f, zero, li, hh);
     const int row0 = kb + 32 * wave;
-    lds_rows_to_buffer<D, E>(kt, dkg + (int64_t)row0 * sdkn, sdkn, N - row0, lane, p.dl);
-    lds_rows_to_buffer<D, E>(vt, dvg + (int64_t)row0 * sdvn, sdvn, N - row0, lane, p.dl);
+    lds_rows_to_buffer<D, E>(kt, dkg + (int64_t)row0 * sdkn, sdkn, N - row0, lane, dl);
+    lds_rows_to_buffer<D, E>(vt, dvg + (int64_t)row0 * sdvn, sdvn, N - row0, lane, dl);
   }
   prefetched = !DROPOUT && has_next;
   }  // block
@@ -745,6 +748,9 @@ void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) E sv1[TILE];
 
   const int N = p.N;
+  // Head size of the tensors: columns [dl, D) are zero-padded on chip.  The
+  // kernels with compile-time strides run only at dl = D.
+  const int dl = CONTIG ? D : p.dl;
   const int nqb = p.num_blocks;
   // Causal: a workgroup takes query blocks nqb-1-w and w in turn (equal work).
   // SPLIT: p.splits workgroups per such unit, workgroup s taking share s of
@@ -798,8 +804,8 @@ void bwd_dq_kernel(BwdParams p) {
   // The copies cover the tiles [0, nkb) only: copies past them (issued without
   // a branch) read zeros without touching memory.
   const int krows = min(nkb * BN, N);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, rows_bytes(krows, skn, p.dl, ES));
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, rows_bytes(krows, svn, p.dl, ES));
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, rows_bytes(krows, skn, dl, ES));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, rows_bytes(krows, svn, dl, ES));
   // Copy i of this lane fills chunk slot (i * NW + wave) * 64 + lane, i.e.
   // row i * COPY_ROWS + wave * 64 / CHUNKS + lane / CHUNKS, chunk
   // lane % CHUNKS.  The swizzle depends on the row mod 16, which does not
@@ -815,8 +821,8 @@ void bwd_dq_kernel(BwdParams p) {
     const int r = wrow + lane / C::CHUNKS, pc = lane % C::CHUNKS;
     crow = lane / C::CHUNKS;
     lch = (pc ^ swz<D>(r)) * 8;  // first column of the chunk this lane copies
-    ldl_k = lch < p.dl ? (uint32_t)(crow * skn + lch) * ES : kPoison;
-    ldl_v = lch < p.dl ? (uint32_t)(crow * svn + lch) * ES : kPoison;
+    ldl_k = lch < dl ? (uint32_t)(crow * skn + lch) * ES : kPoison;
+    ldl_v = lch < dl ? (uint32_t)(crow * svn + lch) * ES : kPoison;
   }
   // Per-lane offsets of tile jt's first K and V copies (formed once per tile).
   const uint32_t krb = (uint32_t)skn * ES, vrb = (uint32_t)svn * ES;
@@ -854,10 +860,10 @@ void bwd_dq_kernel(BwdParams p) {
     // past N read as zero); every wave then reads its rows into registers.
     // Loading them straight into registers, a lane per row, cost more than
     // this whole round trip.  The stages are free again after the barrier.
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qg, rows_bytes(N, sqn, p.dl, ES));
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(dog, rows_bytes(N, son_, p.dl, ES));
-    const uint32_t ldl_q = lch < p.dl ? (uint32_t)(crow * sqn + lch) * ES : kPoison;
-    const uint32_t ldl_o = lch < p.dl ? (uint32_t)(crow * son_ + lch) * ES : kPoison;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qg, rows_bytes(N, sqn, dl, ES));
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(dog, rows_bytes(N, son_, dl, ES));
+    const uint32_t ldl_q = lch < dl ? (uint32_t)(crow * sqn + lch) * ES : kPoison;
+    const uint32_t ldl_o = lch < dl ? (uint32_t)(crow * son_ + lch) * ES : kPoison;
     const uint32_t qrb = (uint32_t)sqn * ES, orb = (uint32_t)son_ * ES;
     const uint32_t qb = tile_offset<CONTIG>(ldl_q, q0 + wrow, qrb), ob = tile_offset<CONTIG>(ldl_o, q0 + wrow, orb);
 #pragma unroll
@@ -887,7 +893,7 @@ void bwd_dq_kernel(BwdParams p) {
     const E* orow = og + (int64_t)qi * son_o + 8 * hh;
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      if (16 * c + 8 * hh < p.dl) drow = Elem<E>::dot8(*(const V8*)(orow + 16 * c), oreg[c], drow);
+      if (16 * c + 8 * hh < dl) drow = Elem<E>::dot8(*(const V8*)(orow + 16 * c), oreg[c], drow);
     const float lv = p.lse[(size_t)head * N + qi];
     lrow = lv == -INFINITY ? INFINITY : lv * kLog2e;
   }
@@ -1045,7 +1051,7 @@ void bwd_dq_kernel(BwdParams p) {
     const int qw = q0 + wave * 32;
     E* qt = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
     acc_rows_to_lds<D, E>(qt, qacc, p.scale, false, li, hh);
-    lds_rows_to_buffer<D, E>(qt, dqg + (int64_t)qw * sdqn, sdqn, N - qw, lane, p.dl);
+    lds_rows_to_buffer<D, E>(qt, dqg + (int64_t)qw * sdqn, sdqn, N - qw, lane, dl);
   }
   }  // item
 }

@@ -104,6 +104,9 @@ void fwd_kernel(FwdParams p) {
   auto vbuf = [&](int stage) -> E* { return stage ? sv1 : sv0; };
 
   const int N = p.N;
+  // Head size of the tensors: columns [dl, D) are zero-padded on chip.  The
+  // kernels with compile-time strides run only at dl = D.
+  const int dl = CONTIG ? D : p.dl;
   const int nqb = p.num_qblocks;
   // With a causal mask query block b costs b + 1 key tiles: a workgroup takes
   // blocks nqb-1-w and w in turn, so every workgroup does the same work (no
@@ -159,14 +162,14 @@ void fwd_kernel(FwdParams p) {
   // The copies cover the tiles [0, nkb) only: copies past them (issued without
   // a branch) read zeros without touching memory.
   const int krows = min((jt0 + nkb) * BN, N);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, rows_bytes(krows, skn, p.dl, ES));
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, rows_bytes(krows, svn, p.dl, ES));
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, rows_bytes(krows, skn, dl, ES));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, rows_bytes(krows, svn, dl, ES));
 
   // Q^T as the B operand of S^T = K Q^T: lane holds Q[qi][16c + 8hh .. +7].
   V8 qreg[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    if (qi < N && 16 * c + 8 * hh < p.dl) {
+    if (qi < N && 16 * c + 8 * hh < dl) {
       qreg[c] = *(const V8*)(qg + (int64_t)qi * sqn + 16 * c + 8 * hh);
     } else {
 #pragma unroll
@@ -185,8 +188,8 @@ void fwd_kernel(FwdParams p) {
   {
     const int r = wave * 64 / C::CHUNKS + lane / C::CHUNKS, pc = lane % C::CHUNKS;
     const int lch = (pc ^ swz<D>(r)) * 8;  // first column of the chunk this lane copies
-    kld0 = lch < p.dl ? (uint32_t)(r * skn + lch) * ES : kPoison;
-    vld0 = lch < p.dl ? (uint32_t)(r * svn + lch) * ES : kPoison;
+    kld0 = lch < dl ? (uint32_t)(r * skn + lch) * ES : kPoison;
+    vld0 = lch < dl ? (uint32_t)(r * svn + lch) * ES : kPoison;
   }
   // Row strides in bytes, and the byte step between copy rounds.
   const uint32_t krb = (uint32_t)skn * ES, vrb = (uint32_t)svn * ES;
@@ -493,7 +496,7 @@ void fwd_kernel(FwdParams p) {
     {
       E* ot = ((wave >> 1) ? sk1 : sk0) + (wave & 1) * 32 * D;
       acc_rows_to_lds<D, E>(ot, oacc, inv, false, li, hh);
-      lds_rows_to_buffer<D, E>(ot, og + (int64_t)qw * son, son, N - qw, lane, p.dl);
+      lds_rows_to_buffer<D, E>(ot, og + (int64_t)qw * son, son, N - qw, lane, dl);
     }
     if (qi < N && hh == 0) p.lse[(size_t)head * N + qi] = lse_out;
   }
@@ -570,8 +573,10 @@ hipError_t dispatch(const FwdParams& p, int heads, bool causal, bool dropout, hi
 }
 
 // Rows d elements apart in every tensor (the batch and head strides are free).
+// Every row stride equals the kernel width and the head size fills it (the
+// compile-time-stride kernels do not pad).
 bool rows_contiguous(const FwdParams& p, int d) {
-  return p.sq.n == d && p.sk.n == d && p.sv.n == d && p.so.n == d;
+  return p.dl == d && p.sq.n == d && p.sk.n == d && p.sv.n == d && p.so.n == d;
 }
 
 // The split path (small batch x heads) keeps run-time strides only.
