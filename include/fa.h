@@ -218,6 +218,38 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         hipStream_t stream);
 
 /*
+ * Packed batches in one launch per pass: the varlen entry points above with
+ * the offsets in DEVICE memory, as a training loop holds them.
+ *   cu_seqlens    device int32 array of num_seqs + 1 offsets (cu_seqlens[0]
+ *                 = 0, non-decreasing); read by the kernels, not checked.
+ *   max_len       the longest sequence, >= every cu_seqlens[b+1] -
+ *                 cu_seqlens[b] (rows past max_len of a longer sequence are
+ *                 neither read nor written).
+ *   total_tokens  cu_seqlens[num_seqs] (the rows the strides must cover).
+ * One launch covers every sequence: workgroup (b, h, query block) reads its
+ * sequence's first row and length from cu_seqlens, and blocks past the
+ * length exit at once.  The MFMA kernels only: FA_BF16 / FA_F16 at d in
+ * {32, 64, 96, 128} (else FA_ERR_UNSUPPORTED; the host-offset entry points
+ * take every type and head size).  Everything else (strides, LSE layout,
+ * masks, the dropout counter with b as the batch index) as fa_fwd_varlen /
+ * fa_bwd_varlen, and the same results bit for bit.  The backward's workspace:
+ * fa_bwd_varlen_device_workspace_size() bytes (the per-row terms of every
+ * token and head).
+ */
+fa_status fa_fwd_varlen_device(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const fa_strides* strides, const int32_t* cu_seqlens, int num_seqs,
+                               int max_len, int total_tokens, int H, int d, fa_dtype dtype,
+                               float scale, int causal, float dropout_p, uint64_t seed,
+                               hipStream_t stream);
+size_t fa_bwd_varlen_device_workspace_size(int total_tokens, int H, int d, fa_dtype dtype);
+fa_status fa_bwd_varlen_device(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               const fa_strides* strides, const int32_t* cu_seqlens, int num_seqs,
+                               int max_len, int total_tokens, int H, int d, fa_dtype dtype,
+                               float scale, int causal, float dropout_p, uint64_t seed,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for these sizes: two fp32 [B, H, N]
  * row arrays, D_i = sum_k dO_ik O_ik and LSE_i * log2(e), each padded to a
  * multiple of 256 bytes.

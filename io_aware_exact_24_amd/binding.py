@@ -19,7 +19,8 @@ FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_split", "fa_fwd_split_workspace_size",
            "fa_bwd_noalloc", "fa_fwd_strided", "fa_bwd_strided", "fa_fwd_varlen", "fa_bwd_varlen",
-           "fa_bwd_varlen_workspace_size", "fa_bwd_split", "fa_bwd_split_workspace_size")
+           "fa_bwd_varlen_workspace_size", "fa_bwd_split", "fa_bwd_split_workspace_size",
+           "fa_fwd_varlen_device", "fa_bwd_varlen_device", "fa_bwd_varlen_device_workspace_size")
 FA_MAX_SPLITS = 64
 FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -93,6 +94,14 @@ def load_library():
     lib.fa_bwd_strided.restype = i
     lib.fa_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sp, i, i, i, i, i, f, i, vp,
                                    f, u64, vp, sz, vp]
+    lib.fa_fwd_varlen_device.restype = i
+    lib.fa_fwd_varlen_device.argtypes = [vp, vp, vp, vp, vp, sp, vp, i, i, i, i, i, i, f, i, f, u64,
+                                         vp]
+    lib.fa_bwd_varlen_device_workspace_size.restype = sz
+    lib.fa_bwd_varlen_device_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_bwd_varlen_device.restype = i
+    lib.fa_bwd_varlen_device.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sp, vp, i, i, i, i, i,
+                                         i, f, i, f, u64, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -548,4 +557,90 @@ def backward(q, k, v, o, dout, lse, scale, causal=False, key_lens=None, dropout_
     else:
         fa_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, key_lens, dropout_p, seed,
                        workspace, stream)
+    return dq, dk, dv
+
+
+def _cu_device(cu_seqlens, device):
+    """Device int32 offsets (a CUDA tensor is used as it is) and the sequence count."""
+    import torch
+
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens: expected a contiguous int32 tensor")
+        return cu_seqlens, cu_seqlens.numel() - 1
+    t = torch.as_tensor(cu_seqlens, dtype=torch.int32).to(device)
+    return t, t.numel() - 1
+
+
+def fa_fwd_varlen_device(q, k, v, o, lse, cu_seqlens, max_len, scale, causal=False, dropout_p=0.0,
+                         seed=0, stream=None):
+    """fa_fwd_varlen_device: fa_fwd_varlen with the offsets on the device (one
+    launch for every sequence); max_len >= the longest sequence."""
+    import torch
+
+    lib = load_library()
+    T, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_packed(t, q.shape, q.dtype, q.device, name)
+    if lse.dtype != torch.float32 or lse.numel() != H * T or not lse.is_contiguous():
+        raise ValueError("lse: expected a contiguous fp32 tensor of H * T elements")
+    cu, n = _cu_device(cu_seqlens, q.device)
+    st = lib.fa_fwd_varlen_device(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  _packed_strides((q, k, v, o)), _ptr(cu), n, int(max_len), T, H, d,
+                                  _dtype_code(q), float(scale), int(bool(causal)), float(dropout_p),
+                                  int(seed), _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_varlen_device")
+
+
+def fa_bwd_varlen_device_workspace_size(total_tokens, H, d, dtype_code=FA_BF16):
+    return int(load_library().fa_bwd_varlen_device_workspace_size(total_tokens, H, d, dtype_code))
+
+
+def fa_bwd_varlen_device(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, max_len, scale,
+                         causal=False, dropout_p=0.0, seed=0, workspace=None, stream=None):
+    """fa_bwd_varlen_device: fa_bwd_varlen with the offsets on the device."""
+    lib = load_library()
+    T, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _check_packed(t, q.shape, q.dtype, q.device, name)
+    if workspace is None:
+        raise ValueError("fa_bwd_varlen_device needs a workspace tensor")
+    cu, n = _cu_device(cu_seqlens, q.device)
+    st = lib.fa_bwd_varlen_device(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                  _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _packed_strides((q, k, v, o, dout, dq, dk, dv)), _ptr(cu), n,
+                                  int(max_len), T, H, d, _dtype_code(q), float(scale),
+                                  int(bool(causal)), float(dropout_p), int(seed), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_varlen_device")
+
+
+def forward_varlen_device(q, k, v, cu_seqlens, max_len, scale, causal=False, dropout_p=0.0, seed=0,
+                          stream=None):
+    """Allocate O (in q's layout) and LSE and call fa_fwd_varlen_device."""
+    import torch
+
+    T, H, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(H * T, dtype=torch.float32, device=q.device)
+    fa_fwd_varlen_device(q, k, v, o, lse, cu_seqlens, max_len, scale, causal, dropout_p, seed,
+                         stream)
+    return o, lse
+
+
+def backward_varlen_device(q, k, v, o, dout, lse, cu_seqlens, max_len, scale, causal=False,
+                           dropout_p=0.0, seed=0, stream=None):
+    """Allocate dQ, dK, dV and the workspace and call fa_bwd_varlen_device."""
+    import torch
+
+    T, H, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = fa_bwd_varlen_device_workspace_size(T, H, d, _dtype_code(q))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    fa_bwd_varlen_device(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, max_len, scale, causal,
+                         dropout_p, seed, ws, stream)
     return dq, dk, dv

@@ -116,7 +116,9 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
                   const fa_strides* strides, int B, int H, int N, int d, fa_dtype dtype,
                   float scale, int causal, const int32_t* key_lens, float dropout_p, uint64_t seed,
                   int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                  int b0 = 0) {
+                  int b0 = 0, const int32_t* cu = nullptr) {
+  // cu: device offsets of packed sequences (B of them, N = the longest); the
+  // caller has checked the strides by the packed-tensor rules.
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
     return FA_ERR_INVALID_ARG;
   if (key_lens != nullptr && ((uintptr_t)key_lens & 3u) != 0) return FA_ERR_INVALID_ARG;
@@ -125,12 +127,12 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (!valid_dropout(dropout_p)) return FA_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
   if (!fa::generic_head_size(d)) return FA_ERR_UNSUPPORTED;
-  if (strides != nullptr) {
+  if (strides != nullptr && cu == nullptr) {
     for (int t = 0; t < 4; ++t) {
       const fa_status st = check_strides(strides[t], B, H, N, d, dtype, t == 3);
       if (st != FA_OK) return st;
     }
-  } else if (!head_bytes_fit(N, d, dtype)) {
+  } else if (strides == nullptr && !head_bytes_fit(N, d, dtype)) {
     return FA_ERR_UNSUPPORTED;
   }
   if (dtype == FA_F32 && dropout_p > 0.0f) return FA_ERR_UNSUPPORTED;
@@ -164,6 +166,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
   a.drop_scale = drop_scale(dropout_p);
   a.seed = seed;
   a.b0 = b0;
+  a.cu = cu;
   if (num_splits > 0) {
     const size_t rows = (size_t)B * H * N;
     a.num_splits = num_splits;
@@ -171,7 +174,9 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     a.lsepart = (float*)((char*)workspace + pad256((size_t)num_splits * rows * d * 4));
   }
   hipError_t e;
-  if (mfma_path(dtype, d) || padded_path(dtype, d, N, {a.sq.n, a.sk.n, a.sv.n, a.so.n}))
+  const bool mfma = mfma_path(dtype, d) || padded_path(dtype, d, N, {a.sq.n, a.sk.n, a.sv.n, a.so.n});
+  if (cu != nullptr && !mfma) return FA_ERR_UNSUPPORTED;  // device offsets: MFMA kernels only
+  if (mfma)
     e = fa::launch_fwd_16(a, stream);
   else
     e = fa::launch_fwd_generic(a, (int)dtype, stream);
@@ -267,7 +272,11 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
                   int H, int N, int d, fa_dtype dtype, float scale, int causal,
                   const int32_t* key_lens, float dropout_p, uint64_t seed, void* workspace,
                   int stages, hipStream_t stream, int b0 = 0, int num_splits = 0,
-                  float* dqp = nullptr, float* dkp = nullptr, float* dvp = nullptr) {
+                  float* dqp = nullptr, float* dkp = nullptr, float* dvp = nullptr,
+                  const int32_t* cu = nullptr, int64_t cu_rows = 0) {
+  // cu: device offsets of packed sequences (B of them, N = the longest) whose
+  // H * cu_rows per-row terms fill the workspace; the caller has checked the
+  // rest.
   fa::BwdArgs a;
   a.fp16 = dtype == FA_F16;
   a.q = q;
@@ -293,7 +302,8 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.b0 = b0;
   // workspace: D, then LSE * log2(e)
   a.delta = (float*)workspace;
-  a.lse2 = (float*)((char*)workspace + row_array_bytes(B, H, N));
+  a.lse2 = (float*)((char*)workspace + (cu ? pad256((size_t)H * cu_rows * 4) : row_array_bytes(B, H, N)));
+  a.cu = cu;
   a.num_splits = num_splits;
   a.dqp = dqp;
   a.dkp = dkp;
@@ -303,6 +313,7 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   const bool mfma = mfma_path(dtype, d) ||
                     padded_path(dtype, d, N, {a.sq.n, a.sk.n, a.sv.n, a.so.n, a.sdo.n, a.sdq.n, a.sdk.n,
                                               a.sdv.n});
+  if (cu != nullptr && !mfma) return FA_ERR_UNSUPPORTED;  // device offsets: MFMA kernels only
   const hipError_t e = mfma ? fa::launch_bwd_16(a, stages, stream)
                             : fa::launch_bwd_generic(a, (int)dtype, stages, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -522,6 +533,78 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
     if (st != FA_OK) return st;
   }
   return FA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Arguments of the device-offset entry points: offsets on the device, counts
+// and the longest length from the caller.  Strides as for the host-offset
+// ones, with the longest sequence for the 32-bit span.
+fa_status check_packed_dev(const int32_t* cu, int num_seqs, int max_len, int total, int H, int d,
+                           fa_dtype dtype, float scale, float dropout_p) {
+  if (cu == nullptr || ((uintptr_t)cu & 3u) != 0) return FA_ERR_INVALID_ARG;
+  if (num_seqs < 1 || max_len < 0 || total < 0 || H <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale <= 0.0f) return FA_ERR_INVALID_ARG;
+  if (!valid_dropout(dropout_p)) return FA_ERR_INVALID_ARG;
+  if (!fa::generic_head_size(d)) return FA_ERR_UNSUPPORTED;
+  // one launch needs the MFMA kernels (16-bit, d = 32 .. 128)
+  if (!is16(dtype) || d > 128) return FA_ERR_UNSUPPORTED;
+  if (max_len > 0 && elems(num_seqs, H, max_len, d) < 0) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_varlen_device(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const fa_strides* strides, const int32_t* cu_seqlens, int num_seqs,
+                               int max_len, int total_tokens, int H, int d, fa_dtype dtype,
+                               float scale, int causal, float dropout_p, uint64_t seed,
+                               hipStream_t stream) {
+  fa_status st = check_packed_dev(cu_seqlens, num_seqs, max_len, total_tokens, H, d, dtype, scale,
+                                  dropout_p);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  fa_strides s[4];
+  st = packed_strides(strides, 4, 3, H, total_tokens, max_len, d, dtype, s);
+  if (st != FA_OK) return st;
+  if (max_len == 0 || total_tokens == 0) return FA_OK;
+  return run_fwd(q, k, v, o, lse, s, num_seqs, H, max_len, d, dtype, scale, causal, nullptr,
+                 dropout_p, seed, 0, nullptr, 0, stream, 0, cu_seqlens);
+}
+
+size_t fa_bwd_varlen_device_workspace_size(int total_tokens, int H, int d, fa_dtype dtype) {
+  if (total_tokens < 0 || H <= 0 || !valid_dtype(dtype) || !fa::generic_head_size(d)) return 0;
+  if (elems(1, H, total_tokens, d) < 0) return 0;
+  return 2 * pad256((size_t)H * total_tokens * 4);
+}
+
+fa_status fa_bwd_varlen_device(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               const fa_strides* strides, const int32_t* cu_seqlens, int num_seqs,
+                               int max_len, int total_tokens, int H, int d, fa_dtype dtype,
+                               float scale, int causal, float dropout_p, uint64_t seed,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fa_status st = check_packed_dev(cu_seqlens, num_seqs, max_len, total_tokens, H, d, dtype, scale,
+                                  dropout_p);
+  if (st != FA_OK) return st;
+  for (const void* ptr : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(ptr)) return FA_ERR_INVALID_ARG;
+  if (!aligned4(lse) || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_bwd_varlen_device_workspace_size(total_tokens, H, d, dtype))
+    return FA_ERR_INVALID_ARG;
+  fa_strides s[8];
+  st = packed_strides(strides, 8, 5, H, total_tokens, max_len, d, dtype, s);
+  if (st != FA_OK) return st;
+  if (max_len == 0 || total_tokens == 0) return FA_OK;
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, s, num_seqs, H, max_len, d, dtype, scale,
+                 causal, nullptr, dropout_p, seed, workspace, fa::kBwdAll, stream, 0, 0, nullptr,
+                 nullptr, nullptr, cu_seqlens, total_tokens);
 }
 
 }  // extern "C"

@@ -27,6 +27,7 @@ hipError_t launch_bwd_16(const BwdArgs& a, int stages, hipStream_t s) {
   p.dk = a.dk;
   p.dv = a.dv;
   p.key_lens = a.key_lens;
+  p.cu = a.cu;
   p.H = a.H;
   p.N = a.N;
   p.dl = a.d;

@@ -64,6 +64,10 @@ struct BwdParams {
   // element strides (batch, head, row) of each tensor; d is contiguous
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   const int32_t* key_lens;
+  // Packed sequences (nullptr otherwise): batch entry b is rows [cu[b],
+  // cu[b+1]) of every tensor (at most N of them; the batch strides are 0); its
+  // LSE, D and LSE * log2(e) are the [H, len] blocks at H * cu[b].
+  const int32_t* cu;
   int H, N, num_blocks;
   int dl;  // head size of the tensors, <= D: columns [dl, D) read as zero and are not written
   int b0;  // added to the batch index in the dropout counter
@@ -208,7 +212,6 @@ void bwd_dkdv_kernel(BwdParams p) {
     return S == 0 ? sd0 : S == 1 ? sd1 : sd2;
   };
 
-  const int N = p.N;
   // Head size of the tensors: columns [dl, D) are zero-padded on chip.  The
   // kernels with compile-time strides run only at dl = D.
   const int dl = CONTIG ? D : p.dl;
@@ -244,7 +247,19 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int w = pu - head_ * per_head;
     jb_ = ss == 0 ? w : nb - 1 - w;
   };
-  const int nit = (N + BQ - 1) / BQ;
+  // Rows of batch entry b_: n_, from row r0_ on (packed sequences: its own
+  // length and first row).
+  auto rows_of = [&](int b_, int& n_, int64_t& r0_) {
+    n_ = p.N;
+    r0_ = 0;
+    if (p.cu) {
+      // wave-uniform values loaded from memory: readfirstlane keeps them in
+      // scalar registers, so the buffer descriptors built from them stay
+      // scalar (otherwise every buffer access becomes a loop over lanes)
+      r0_ = __builtin_amdgcn_readfirstlane(p.cu[b_]);
+      n_ = min(__builtin_amdgcn_readfirstlane(p.cu[b_ + 1]) - (int)r0_, p.N);
+    }
+  };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
@@ -257,6 +272,13 @@ void bwd_dkdv_kernel(BwdParams p) {
   started = true;
   int head, jb;
   block_of(u, sub, head, jb);
+  const int bi = head / p.H, hi = head - bi * p.H;
+  int N;
+  int64_t r0;
+  rows_of(bi, N, r0);
+  // index of row 0's LSE * log2(e) and D
+  const size_t lrow0 = p.cu ? (size_t)r0 * p.H + (size_t)hi * N : (size_t)head * N;
+  const int nit = (N + BQ - 1) / BQ;
   // Query tiles [tlo, thi) of this visit.
   int tlo = CAUSAL ? jb * (BK / BQ) : 0, thi = nit;
   if constexpr (SPLIT) {
@@ -290,7 +312,6 @@ void bwd_dkdv_kernel(BwdParams p) {
   const bool has_next = u < uend;
   int nhead = head, njb = jb;
   if (has_next) block_of(u, sub, nhead, njb);
-  const int bi = head / p.H, hi = head - bi * p.H;
   const int kb = jb * BK;             // first key of the workgroup
   const int key = kb + 32 * wave + li;  // this lane's key (column of S)
 
@@ -298,10 +319,10 @@ void bwd_dkdv_kernel(BwdParams p) {
   if (p.key_lens) L = min(max(p.key_lens[bi], 0), N);
 
   // (b, h) slices through per-tensor strides
-  const E* qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h);
-  const E* dog = (const E*)p.dout + (bi * p.sdo.b + hi * p.sdo.h);
-  E* dkg = (E*)p.dk + (bi * p.sdk.b + hi * p.sdk.h);
-  E* dvg = (E*)p.dv + (bi * p.sdv.b + hi * p.sdv.h);
+  const E* qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h + r0 * p.sq.n);
+  const E* dog = (const E*)p.dout + (bi * p.sdo.b + hi * p.sdo.h + r0 * p.sdo.n);
+  E* dkg = (E*)p.dk + (bi * p.sdk.b + hi * p.sdk.h + r0 * p.sdk.n);
+  E* dvg = (E*)p.dv + (bi * p.sdv.b + hi * p.sdv.h + r0 * p.sdv.n);
 
   // dV^T / dK^T tile u, register r -> d = 32u + 8(r/4) + 4hh + r%4; the first
   // product into each defines it.
@@ -346,8 +367,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int sdkn = CONTIG ? D : (int)p.sdk.n, sdvn = CONTIG ? D : (int)p.sdv.n;
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qg, rows_bytes(N, sqn, dl, ES));
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(dog, rows_bytes(N, son_, dl, ES));
-  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lse2 + (size_t)head * N, (uint32_t)N * 4);
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.delta + (size_t)head * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.lse2 + lrow0, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.delta + lrow0, (uint32_t)N * 4);
   // Copy i of this lane fills chunk slot (i * NW + wave) * 64 + lane: row
   // r = i * COPY_ROWS + wave * 64 / CHUNKS + lane / CHUNKS, chunk
   // lane % CHUNKS.  The swizzle of r depends on r mod 16 only, which does not
@@ -370,11 +391,14 @@ void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NFETCH = KC + 2 * C::LOADS;
   auto fetch_kv = [&](int head_, int kb_, V8 (&kdst)[KC]) __attribute__((always_inline)) {
     const int b_ = head_ / p.H, h_ = head_ - b_ * p.H;
+    int n_;  // the rows of that block's batch entry (another one than this block's, possibly)
+    int64_t r0_;
+    rows_of(b_, n_, r0_);
     const __amdgpu_buffer_rsrc_t krs =
-        make_rsrc((const E*)p.k + (b_ * p.sk.b + h_ * p.sk.h), rows_bytes(N, skn, dl, ES));
+        make_rsrc((const E*)p.k + (b_ * p.sk.b + h_ * p.sk.h + r0_ * p.sk.n), rows_bytes(n_, skn, dl, ES));
     const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc((const E*)p.v + (b_ * p.sv.b + h_ * p.sv.h), rows_bytes(N, svn, dl, ES));
-    const uint32_t krow = (uint32_t)(min(kb_ + 32 * wave + li, N) * skn) * ES + (uint32_t)(16 * hh);
+        make_rsrc((const E*)p.v + (b_ * p.sv.b + h_ * p.sv.h + r0_ * p.sv.n), rows_bytes(n_, svn, dl, ES));
+    const uint32_t krow = (uint32_t)(min(kb_ + 32 * wave + li, n_) * skn) * ES + (uint32_t)(16 * hh);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       kdst[c] = __builtin_bit_cast(
@@ -747,7 +771,6 @@ void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) E sv0[TILE];
   __shared__ __attribute__((aligned(1024))) E sv1[TILE];
 
-  const int N = p.N;
   // Head size of the tensors: columns [dl, D) are zero-padded on chip.  The
   // kernels with compile-time strides run only at dl = D.
   const int dl = CONTIG ? D : p.dl;
@@ -766,17 +789,30 @@ void bwd_dq_kernel(BwdParams p) {
   const int w = lid - head * per_head;
   const int nitems = CAUSAL && w != nqb - 1 - w ? 2 : 1;
   const int bi = head / p.H, hi = head - bi * p.H;
+  // Rows of this batch entry: N, from row r0 on (packed sequences: its own
+  // length and first row).
+  int N = p.N;
+  int64_t r0 = 0;
+  if (p.cu) {
+    // wave-uniform values loaded from memory: readfirstlane keeps them in
+    // scalar registers, so the buffer descriptors built from them stay
+    // scalar (otherwise every buffer access becomes a loop over lanes)
+    r0 = __builtin_amdgcn_readfirstlane(p.cu[bi]);
+    N = min(__builtin_amdgcn_readfirstlane(p.cu[bi + 1]) - (int)r0, p.N);
+  }
+  // index of row 0's LSE, D and LSE * log2(e)
+  const size_t lrow0 = p.cu ? (size_t)r0 * p.H + (size_t)hi * N : (size_t)head * N;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
   // (b, h) slices through per-tensor strides (both items of a workgroup are
   // in the same head)
-  const E* qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h);
-  const E* kg = (const E*)p.k + (bi * p.sk.b + hi * p.sk.h);
-  const E* vg = (const E*)p.v + (bi * p.sv.b + hi * p.sv.h);
-  const E* dog = (const E*)p.dout + (bi * p.sdo.b + hi * p.sdo.h);
-  const E* og = (const E*)p.o + (bi * p.so.b + hi * p.so.h);
-  E* dqg = (E*)p.dq + (bi * p.sdq.b + hi * p.sdq.h);
+  const E* qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h + r0 * p.sq.n);
+  const E* kg = (const E*)p.k + (bi * p.sk.b + hi * p.sk.h + r0 * p.sk.n);
+  const E* vg = (const E*)p.v + (bi * p.sv.b + hi * p.sv.h + r0 * p.sv.n);
+  const E* dog = (const E*)p.dout + (bi * p.sdo.b + hi * p.sdo.h + r0 * p.sdo.n);
+  const E* og = (const E*)p.o + (bi * p.so.b + hi * p.so.h + r0 * p.so.n);
+  E* dqg = (E*)p.dq + (bi * p.sdq.b + hi * p.sdq.h + r0 * p.sdq.n);
   // Row strides (CONTIG: d, known at compile time).
   const int sqn = CONTIG ? D : (int)p.sq.n, skn = CONTIG ? D : (int)p.sk.n;
   const int svn = CONTIG ? D : (int)p.sv.n, son_ = CONTIG ? D : (int)p.sdo.n;
@@ -785,6 +821,7 @@ void bwd_dq_kernel(BwdParams p) {
   if (item) __syncthreads();  // every wave is done with the first block's tiles
   const int qb = CAUSAL ? (item == 0 ? nqb - 1 - w : w) : w;
   const int q0 = qb * C::BM;
+  if (q0 >= N) continue;  // a packed sequence shorter than the longest
   const int qi = q0 + wave * 32 + li;  // this lane's query
 
   int L = N;
@@ -894,13 +931,13 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       if (16 * c + 8 * hh < dl) drow = Elem<E>::dot8(*(const V8*)(orow + 16 * c), oreg[c], drow);
-    const float lv = p.lse[(size_t)head * N + qi];
+    const float lv = p.lse[lrow0 + qi];
     lrow = lv == -INFINITY ? INFINITY : lv * kLog2e;
   }
   drow = pair_sum(drow);
   if (hh == 0 && qi < N && share == 0) {
-    p.delta[(size_t)head * N + qi] = drow;
-    p.lse2[(size_t)head * N + qi] = lrow;
+    p.delta[lrow0 + qi] = drow;
+    p.lse2[lrow0 + qi] = lrow;
   }
   const int g16 = lane & 15;
   const int trow = 4 * hh + (g16 >> 2);

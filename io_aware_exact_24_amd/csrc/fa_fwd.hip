@@ -44,6 +44,10 @@ struct FwdParams {
   void* o;
   float* lse;  // contiguous [B, H, N]
   const int32_t* key_lens;
+  // Packed sequences (nullptr otherwise): batch entry b is rows [cu[b],
+  // cu[b+1]) of every tensor (at most N of them; the batch strides are 0),
+  // and its LSE the [H, len] block at H * cu[b].
+  const int32_t* cu;
   Strides sq, sk, sv, so;  // element strides (batch, head, row); d is contiguous
   int H, N, num_qblocks;
   int dl;  // head size of the tensors, <= D: columns [dl, D) read as zero and are not written
@@ -103,7 +107,6 @@ void fwd_kernel(FwdParams p) {
   auto kbuf = [&](int stage) -> E* { return stage ? sk1 : sk0; };
   auto vbuf = [&](int stage) -> E* { return stage ? sv1 : sv0; };
 
-  const int N = p.N;
   // Head size of the tensors: columns [dl, D) are zero-padded on chip.  The
   // kernels with compile-time strides run only at dl = D.
   const int dl = CONTIG ? D : p.dl;
@@ -119,15 +122,27 @@ void fwd_kernel(FwdParams p) {
   const int w = lid - head * per_head;
   const int nitems = !SPLIT && CAUSAL && w != nqb - 1 - w ? 2 : 1;
   const int bi = head / p.H, hi = head - bi * p.H;
+  // Rows of this batch entry: N, from row r0 on (packed sequences: its own
+  // length and first row).
+  int N = p.N;
+  int64_t r0 = 0;
+  if (p.cu) {
+    // wave-uniform values loaded from memory: readfirstlane keeps them in
+    // scalar registers, so the buffer descriptors built from them stay
+    // scalar (otherwise every buffer access becomes a loop over lanes)
+    r0 = __builtin_amdgcn_readfirstlane(p.cu[bi]);
+    N = min(__builtin_amdgcn_readfirstlane(p.cu[bi + 1]) - (int)r0, p.N);
+  }
+  const size_t lse0 = p.cu ? (size_t)r0 * p.H + (size_t)hi * N : (size_t)head * N;  // LSE of row 0
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
   // (b, h) slices through per-tensor strides; rows are p.s?.n elements apart
   // (both items of a workgroup are in the same head).
-  const E* __restrict__ qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h);
-  const E* kg = (const E*)p.k + (bi * p.sk.b + hi * p.sk.h);
-  const E* vg = (const E*)p.v + (bi * p.sv.b + hi * p.sv.h);
-  E* og = (E*)p.o + (bi * p.so.b + hi * p.so.h);
+  const E* __restrict__ qg = (const E*)p.q + (bi * p.sq.b + hi * p.sq.h + r0 * p.sq.n);
+  const E* kg = (const E*)p.k + (bi * p.sk.b + hi * p.sk.h + r0 * p.sk.n);
+  const E* vg = (const E*)p.v + (bi * p.sv.b + hi * p.sv.h + r0 * p.sv.n);
+  E* og = (E*)p.o + (bi * p.so.b + hi * p.so.h + r0 * p.so.n);
   // Row strides; CONTIG: every row is d elements after the previous one, known
   // at compile time, so tile offsets fold into constants.
   const int sqn = CONTIG ? D : (int)p.sq.n, skn = CONTIG ? D : (int)p.sk.n;
@@ -137,6 +152,7 @@ void fwd_kernel(FwdParams p) {
   int qb = CAUSAL ? (item == 0 ? nqb - 1 - w : w) : w;
   if constexpr (SPLIT) qb = CAUSAL ? nqb - 1 - w / p.num_splits : w / p.num_splits;
   const int q0 = qb * C::BM;
+  if (q0 >= N) continue;  // a packed sequence shorter than the longest
   const int qw = q0 + wave * 32;  // first query of this wave
   const int qi = qw + li;         // this lane's query
 
@@ -498,7 +514,7 @@ void fwd_kernel(FwdParams p) {
       acc_rows_to_lds<D, E>(ot, oacc, inv, false, li, hh);
       lds_rows_to_buffer<D, E>(ot, og + (int64_t)qw * son, son, N - qw, lane, dl);
     }
-    if (qi < N && hh == 0) p.lse[(size_t)head * N + qi] = lse_out;
+    if (qi < N && hh == 0) p.lse[lse0 + qi] = lse_out;
   }
   }  // item
 }
@@ -611,6 +627,7 @@ FwdParams make_params(const FwdArgs& a) {
   p.o = a.o;
   p.lse = a.lse;
   p.key_lens = a.key_lens;
+  p.cu = a.cu;
   p.sq = a.sq;
   p.sk = a.sk;
   p.sv = a.sv;

@@ -33,6 +33,9 @@ struct FwdArgs {
   float drop_scale;         // fp32(1 / (1 - p))
   uint64_t seed;
   int b0 = 0;  // batch index of entry 0 in the dropout counter (packed sequences)
+  // Packed sequences in one launch: device offsets, entry b = rows [cu[b],
+  // cu[b+1]) (batch strides 0, N = the longest); nullptr otherwise.
+  const int32_t* cu = nullptr;
   // Split-KV (bf16 only): num_splits > 0 splits each query block's key tiles
   // that many ways into the fp32 workspaces opart [S][B*H][N][d] and
   // lsepart [S][B*H][N], then combines them into o and lse.  0: one pass.
@@ -62,6 +65,7 @@ struct BwdArgs {
   float drop_scale;
   uint64_t seed;
   int b0 = 0;  // batch index of entry 0 in the dropout counter (packed sequences)
+  const int32_t* cu = nullptr;  // packed sequences in one launch (see FwdArgs)
   float* delta;   // workspace: fp32 [B, H, N], D_i = sum_k dO_ik O_ik
   float* lse2;    // workspace: fp32 [B, H, N], LSE_i * log2(e) (+inf for an empty row)
   // Split backward (16-bit, contiguous, d in {64, 128}): num_splits > 0 splits

@@ -439,3 +439,54 @@ def test_varlen_backward_workspace_and_rejects(lib):
     assert call([0, 100, 130], wsb=need - 1) == INVALID
     assert call([0, 100, 90]) == INVALID
     assert call([0, 100, 130], dt=binding.FA_F32, p=0.1) == UNSUPPORTED
+
+
+# ---- fa_fwd_varlen_device / fa_bwd_varlen_device: packed sequences (device offsets)
+
+
+def fwd_vd(lib, n=2, max_len=64, total=100, H=2, d=64, dtype=binding.FA_BF16, p=0.0, strides=None,
+           ptrs=None, cu=P, scale=0.125):
+    ptrs = ptrs or [P] * 5
+    return lib.fa_fwd_varlen_device(*ptrs, strides, cu, n, max_len, total, H, d, dtype, scale, 0, p,
+                                    0, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(cu=None), INVALID), (dict(cu=P + 2), INVALID), (dict(n=0), INVALID),
+    (dict(max_len=-1), INVALID), (dict(total=-1), INVALID), (dict(H=0), INVALID),
+    (dict(dtype=7), INVALID), (dict(scale=0.0), INVALID), (dict(p=1.0), INVALID),
+    (dict(d=48), UNSUPPORTED),
+    # one launch needs the MFMA kernels: 16-bit, d <= 128
+    (dict(dtype=binding.FA_F32), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(ptrs=[P, P, P, P + 8, P]), INVALID), (dict(ptrs=[P, P, P, P, P + 2]), INVALID),
+    # o rows 64 apart with 2 heads: heads overlap the next token's rows
+    (dict(strides=strides_arr([(0, 64, 128)] * 3 + [(0, 64, 64)])), INVALID),
+])
+def test_varlen_device_rejects(lib, kw, expect):
+    assert fwd_vd(lib, **kw) == expect
+
+
+def test_varlen_device_empty_is_a_no_op(lib):
+    # no row at all: nothing to compute and nothing launched
+    assert fwd_vd(lib, max_len=0) == OK
+    assert fwd_vd(lib, total=0) == OK
+
+
+def test_varlen_device_backward_workspace_and_rejects(lib):
+    ws = lib.fa_bwd_varlen_device_workspace_size
+    # D and LSE * log2(e) of every token and head, each padded to 256 bytes
+    assert ws(1000, 3, 64, binding.FA_BF16) == 2 * ((1000 * 3 * 4 + 255) // 256) * 256
+    assert ws(-1, 3, 64, binding.FA_BF16) == 0
+    assert ws(10, 3, 48, binding.FA_BF16) == 0
+    need = ws(100, 2, 64, binding.FA_BF16)
+
+    def call(wsb=need, dt=binding.FA_BF16, d=64, cu=P, n=2, ptrs=None):
+        ptrs = ptrs or [P] * 9
+        return lib.fa_bwd_varlen_device(*ptrs, None, cu, n, 64, 100, 2, d, dt, 0.125, 0, 0.0, 0, P,
+                                        wsb, None)
+    assert call(wsb=need - 1) == INVALID
+    assert call(cu=None) == INVALID
+    assert call(n=0) == INVALID
+    assert call(dt=binding.FA_F32) == UNSUPPORTED
+    assert call(d=256, wsb=1 << 30) == UNSUPPORTED
+    assert call(ptrs=[P] * 6 + [None] + [P] * 2) == INVALID

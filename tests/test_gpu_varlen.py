@@ -104,3 +104,64 @@ def test_varlen_reads_qkv_in_place():
     oc, lsec = binding.forward_varlen(q.contiguous(), k.contiguous(), v.contiguous(), cu, scale, True)
     torch.cuda.synchronize()
     assert torch.equal(o, oc) and torch.equal(lse, lsec)
+
+
+@pytest.mark.parametrize("dt,d,causal,p,max_len", [
+    (torch.bfloat16, 64, True, 0.0, 300),
+    (torch.bfloat16, 128, False, 0.1, 300),
+    (torch.float16, 64, False, 0.0, 512),     # max_len above the longest sequence
+    (torch.bfloat16, 96, True, 0.1, 300),     # padded head size
+    (torch.float16, 32, False, 0.2, 300),     # padded head size
+    (torch.bfloat16, 128, True, 0.0, 301),
+], ids=lambda x: str(x).replace("torch.", ""))
+def test_varlen_device_offsets_equal_host_offsets(dt, d, causal, p, max_len):
+    # One launch over every sequence (offsets on the device) against one
+    # launch per sequence (host offsets): the same tiles of the same kernels,
+    # so every output must be equal bit for bit.
+    H, seed = 3, 0x5EED5
+    cu = np.concatenate([[0], np.cumsum(LENS)]).astype(np.int32)
+    T = int(cu[-1])
+    note(f"varlen device offsets {dt} d={d} causal={causal} p={p} max_len={max_len} lens={LENS}")
+    g = torch.Generator().manual_seed(d + 7)
+    q, k, v, do = (torch.randn(T, H, d, generator=g).to(dt).to(DEV) for _ in range(4))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    cud = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    o1, lse1 = binding.forward_varlen(q, k, v, cu, scale, causal, p, seed)
+    g1 = binding.backward_varlen(q, k, v, o1, do, lse1, cu, scale, causal, p, seed)
+    o2, lse2 = binding.forward_varlen_device(q, k, v, cud, max_len, scale, causal, p, seed)
+    g2 = binding.backward_varlen_device(q, k, v, o1, do, lse1, cud, max_len, scale, causal, p, seed)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2)
+    for name, a, b in zip(("dq", "dk", "dv"), g1, g2):
+        assert torch.equal(a, b), name
+
+
+def test_varlen_device_many_sequences():
+    # 200 sequences of 1 .. 200 tokens in one launch per pass, against the
+    # oracle on a few of them
+    rng = np.random.default_rng(12)
+    lens = rng.integers(1, 201, 200)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H, d = int(cu[-1]), 2, 64
+    note(f"varlen device offsets, {len(lens)} sequences, {T} tokens")
+    g = torch.Generator().manual_seed(13)
+    q, k, v, do = (torch.randn(T, H, d, generator=g).to(torch.bfloat16) for _ in range(4))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    cud = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = binding.forward_varlen_device(qd, kd, vd, cud, int(lens.max()), scale, True)
+    dq, dk, dv = binding.backward_varlen_device(qd, kd, vd, o, dod, lse, cud, int(lens.max()),
+                                                scale, True)
+    torch.cuda.synchronize()
+    for b in (0, 57, 199, int(np.argmax(lens))):
+        t0, n = int(cu[b]), int(lens[b])
+        seq = [t[t0:t0 + n].transpose(0, 1)[None] for t in (q, k, v, do)]
+        ro, rlse = attention_forward(seq[0], seq[1], seq[2], scale, True)
+        rg = attention_backward(seq[0], seq[1], seq[2], seq[3], scale, True)
+        eo = max_abs(f64(o[t0:t0 + n].transpose(0, 1))[None], ro)
+        el = max_abs(f64(lse[H * t0:H * (t0 + n)]).reshape(1, H, n), rlse)
+        errs = [rel_l2(f64(a[t0:t0 + n].transpose(0, 1))[None], r) for a, r in zip((dq, dk, dv), rg)]
+        note(f"  sequence {b} (n={n}): max|dO|={eo:.2e} max|dLSE|={el:.2e} relL2 {max(errs):.2e}")
+        assert eo <= TOL_O and el <= TOL_LSE
+        if n > 1:  # a one-token sequence has exactly zero dQ and dK
+            assert max(errs) <= TOL_GRAD
