@@ -51,9 +51,11 @@ hipError_t launch_bwd_16(const BwdArgs& a, int stages, hipStream_t s) {
   // Head sizes 32 and 96 run on the kernels of width 64 and 128.
   const int width = a.d <= 64 ? 64 : 128;
   const int64_t d = width;
-  // compile-time row strides: every stride equals the width, and no padding
-  const bool contig = a.d == width && p.sq.n == d && p.sk.n == d && p.sv.n == d && p.so.n == d &&
-                      p.sdo.n == d && p.sdq.n == d && p.sdk.n == d && p.sdv.n == d;
+  // compile-time row strides: every stride equals the width, no padding, no
+  // packed sequences
+  const bool contig = a.d == width && a.cu == nullptr && p.sq.n == d && p.sk.n == d &&
+                      p.sv.n == d && p.so.n == d && p.sdo.n == d && p.sdq.n == d && p.sdk.n == d &&
+                      p.sdv.n == d;
   if (stages & kBwdPre) {
     const hipError_t e = launch_bwd_pre(p, a.fp16, width, (int64_t)heads * a.N, s);
     if (e != hipSuccess) return e;

@@ -252,7 +252,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   auto rows_of = [&](int b_, int& n_, int64_t& r0_) {
     n_ = p.N;
     r0_ = 0;
-    if (p.cu) {
+    if (!CONTIG && p.cu) {  // packed sequences run on the run-time-stride kernels
       // wave-uniform values loaded from memory: readfirstlane keeps them in
       // scalar registers, so the buffer descriptors built from them stay
       // scalar (otherwise every buffer access becomes a loop over lanes)
@@ -277,7 +277,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   int64_t r0;
   rows_of(bi, N, r0);
   // index of row 0's LSE * log2(e) and D
-  const size_t lrow0 = p.cu ? (size_t)r0 * p.H + (size_t)hi * N : (size_t)head * N;
+  const size_t lrow0 = !CONTIG && p.cu ? (size_t)r0 * p.H + (size_t)hi * N : (size_t)head * N;
   const int nit = (N + BQ - 1) / BQ;
   // Query tiles [tlo, thi) of this visit.
   int tlo = CAUSAL ? jb * (BK / BQ) : 0, thi = nit;
@@ -793,7 +793,7 @@ void bwd_dq_kernel(BwdParams p) {
   // length and first row).
   int N = p.N;
   int64_t r0 = 0;
-  if (p.cu) {
+  if (!CONTIG && p.cu) {  // packed sequences run on the run-time-stride kernels
     // wave-uniform values loaded from memory: readfirstlane keeps them in
     // scalar registers, so the buffer descriptors built from them stay
     // scalar (otherwise every buffer access becomes a loop over lanes)
@@ -801,7 +801,7 @@ void bwd_dq_kernel(BwdParams p) {
     N = min(__builtin_amdgcn_readfirstlane(p.cu[bi + 1]) - (int)r0, p.N);
   }
   // index of row 0's LSE, D and LSE * log2(e)
-  const size_t lrow0 = p.cu ? (size_t)r0 * p.H + (size_t)hi * N : (size_t)head * N;
+  const size_t lrow0 = !CONTIG && p.cu ? (size_t)r0 * p.H + (size_t)hi * N : (size_t)head * N;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;

@@ -126,14 +126,14 @@ void fwd_kernel(FwdParams p) {
   // length and first row).
   int N = p.N;
   int64_t r0 = 0;
-  if (p.cu) {
+  if (!CONTIG && p.cu) {  // packed sequences run on the run-time-stride kernels
     // wave-uniform values loaded from memory: readfirstlane keeps them in
     // scalar registers, so the buffer descriptors built from them stay
     // scalar (otherwise every buffer access becomes a loop over lanes)
     r0 = __builtin_amdgcn_readfirstlane(p.cu[bi]);
     N = min(__builtin_amdgcn_readfirstlane(p.cu[bi + 1]) - (int)r0, p.N);
   }
-  const size_t lse0 = p.cu ? (size_t)r0 * p.H + (size_t)hi * N : (size_t)head * N;  // LSE of row 0
+  const size_t lse0 = !CONTIG && p.cu ? (size_t)r0 * p.H + (size_t)hi * N : (size_t)head * N;  // LSE of row 0
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
@@ -589,10 +589,12 @@ hipError_t dispatch(const FwdParams& p, int heads, bool causal, bool dropout, hi
 }
 
 // Rows d elements apart in every tensor (the batch and head strides are free).
-// Every row stride equals the kernel width and the head size fills it (the
-// compile-time-stride kernels do not pad).
+// Every row stride equals the kernel width, the head size fills it and the
+// rows are not packed sequences (the compile-time-stride kernels neither pad
+// nor read sequence offsets).
 bool rows_contiguous(const FwdParams& p, int d) {
-  return p.dl == d && p.sq.n == d && p.sk.n == d && p.sv.n == d && p.so.n == d;
+  return p.cu == nullptr && p.dl == d && p.sq.n == d && p.sk.n == d && p.sv.n == d &&
+         p.so.n == d;
 }
 
 // The split path (small batch x heads) keeps run-time strides only.
