@@ -358,7 +358,7 @@ void fwd_kernel(FwdParams p) {
     const E* ks = kbuf(PAR ^ 1);
     auto kread = [&](int i) { return *(const V8*)(ks + koff[i % KC] + (i / KC) * 32 * D); };
     V8 pb[4];
-    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float ps[4];  // partial row sums, each started by its first exponential
     V8 ka[3];
     if constexpr (HAS_NEXT) {
       ka[0] = kread(0);
@@ -389,7 +389,7 @@ void fwd_kernel(FwdParams p) {
         const int k = i * EPA + x, tt = k >> 4, r = k & 15;
         const float e = fast_exp2(fmaf(scur[tt][r], c2, nm));
         scur[tt][r] = e;
-        ps[k & 3] += e;
+        ps[k & 3] = k < 4 ? e : ps[k & 3] + e;
         pin(ps[k & 3]);  // keep the sum here, between this group's MFMAs
       }
       if constexpr (!DROPOUT) {
