@@ -939,6 +939,13 @@ void bwd_dq_kernel(BwdParams p) {
     p.delta[lrow0 + qi] = drow;
     p.lse2[lrow0 + qi] = lrow;
   }
+  // Without dropout (dS = P (Z dP - D) otherwise) and where the registers
+  // allow it (width 64; at 128 the block of 16 spills into the loop), the dP
+  // chains start from -D: the accumulator below, every register this lane's row.
+  constexpr bool NEGD = !DROPOUT && D == 64;
+  f32x16 negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = NEGD ? -drow : 0.0f;
   const int g16 = lane & 15;
   const int trow = 4 * hh + (g16 >> 2);
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
@@ -966,6 +973,8 @@ void bwd_dq_kernel(BwdParams p) {
     __syncthreads();  // tile j resident; every wave is done with tile j-1
 
     // ---- S^T = K Q^T and dP^T = V dO^T: key tile t (32 keys), k-step c.
+    // NEGD: the dP chains start from -D (one row per lane), so they end at
+    // dP - D and dS = P (dP - D) is one multiply.
     f32x16 sacc[2], pacc[2];
     const f32x16 zero = {};
     constexpr int NS = 4 * KC;
@@ -1000,9 +1009,13 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
-        float dp = pacc[t][r];
-        if constexpr (DROPOUT) dp *= dropout_z(p, qi, j * BN + 32 * t + 8 * g + 4 * hh + e, hi, bi);
-        dsb[2 * t + (g >> 1)][4 * (g & 1) + e] = (E)(sacc[t][r] * (dp - drow));
+        if constexpr (NEGD) {
+          dsb[2 * t + (g >> 1)][4 * (g & 1) + e] = (E)(sacc[t][r] * pacc[t][r]);
+        } else {
+          float dp = pacc[t][r];
+          if constexpr (DROPOUT) dp *= dropout_z(p, qi, j * BN + 32 * t + 8 * g + 4 * hh + e, hi, bi);
+          dsb[2 * t + (g >> 1)][4 * (g & 1) + e] = (E)(sacc[t][r] * (dp - drow));
+        }
       }
     };
 #pragma unroll
@@ -1015,7 +1028,8 @@ void bwd_dq_kernel(BwdParams p) {
       if (i + 2 < NS) ring[(i + 2) % 3] = sread(i + 2);
       const int m = i / KC, c = i % KC;
       f32x16& acc = m < 2 ? sacc[m & 1] : pacc[m & 1];
-      acc = Elem<E>::mma(ring[i % 3], m < 2 ? qreg[c] : oreg[c], c == 0 ? zero : acc);
+      acc = Elem<E>::mma(ring[i % 3], m < 2 ? qreg[c] : oreg[c],
+                         c == 0 ? (m >= 2 && NEGD ? negd : zero) : acc);
       if ((c * 4) % KC == 0) {
         const int g = c * 4 / KC;
         if (m == 1) p_elems(0, g);
