@@ -489,7 +489,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int it0 = tlo;  // the first query tile (with a causal mask, a diagonal one unless SPLIT)
 
   // State carried from one tile to the next: P (fp32, masked), dP, P~ packed
-  // as B chunks (chunk kc holds rows 16kc + 8(x/4) + 4hh + x%4 in slot x), the
+  // (with dropout: P times the keep bit, the factor 1/(1-p) left to dV's
+  // epilogue) as B chunks (chunk kc holds rows 16kc + 8(x/4) + 4hh + x%4 in slot x), the
   // dropout keep bits, and the operand ring.
   f32x16 sp[2], sdp[2];
   V8 spb[4];
@@ -515,7 +516,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         // the keep bits of the group's four rows, drawn with the first pair
         if (e + x == 0) zn |= quad_keep4(p, it * BQ + 32 * a + 8 * g + 4 * hh, key, hi, bi) << k;
         const bool keep = (zn >> (k + x)) & 1;
-        pt = keep ? pv * p.drop_scale : 0.0f;
+        pt = keep ? pv : 0.0f;  // the factor 1/(1-p) goes to dV once, in the epilogue
       }
       pb[2 * a + (g >> 1)][4 * (g & 1) + e + x] = (E)pt;
     }
@@ -724,7 +725,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   if constexpr (SPLIT) {
     if (key < N) {
       acc_row_to_f32<D>(dkpart, dkacc, p.scale, key >= L, hh);
-      acc_row_to_f32<D>(dvpart, dvacc, 1.0f, key >= L, hh);
+      acc_row_to_f32<D>(dvpart, dvacc, DROPOUT ? p.drop_scale : 1.0f, key >= L, hh);
     }
   } else {
     __syncthreads();
@@ -732,7 +733,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     E* kt = ((wave >> 1) ? so0 : sq0) + (wave & 1) * 32 * D;
     E* vt = ((wave >> 1) ? so1 : sq1) + (wave & 1) * 32 * D;
     acc_rows_to_lds<D, E>(kt, dkacc, p.scale, zero, li, hh);
-    acc_rows_to_lds<D, E>(vt, dvacc, 1.0f, zero, li, hh);
+    acc_rows_to_lds<D, E>(vt, dvacc, DROPOUT ? p.drop_scale : 1.0f, zero, li, hh);
     const int row0 = kb + 32 * wave;
     lds_rows_to_buffer<D, E>(kt, dkg + (int64_t)row0 * sdkn, sdkn, N - row0, lane, dl);
     lds_rows_to_buffer<D, E>(vt, dvg + (int64_t)row0 * sdvn, sdvn, N - row0, lane, dl);

@@ -413,13 +413,21 @@ void fwd_kernel(FwdParams p) {
           const uint32_t key4 = (uint32_t)((jt0 + j) * BN + 32 * t + 8 * g + 4 * hh);
           const u32x4 w = philox(key4 >> 2, (uint32_t)qi, (uint32_t)hi, (uint32_t)(bi + p.b0), p.seed_lo,
                                  p.seed_hi);
+          // dropped keys contribute zero; the kept ones' factor 1/(1-p) is
+          // applied once, to the normalised output
 #pragma unroll
           for (int x = 0; x < 4; ++x)
-            scur[t][4 * g + x] =
-                (w[x] >= p.drop_threshold) ? scur[t][4 * g + x] * p.drop_scale : 0.0f;
+            scur[t][4 * g + x] = (w[x] >= p.drop_threshold) ? scur[t][4 * g + x] : 0.0f;
         }
+      // pairs converted together (one packed conversion each)
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      typedef E e2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-      for (int k = 0; k < 32; ++k) pb[k >> 3][k & 7] = (E)scur[k >> 4][k & 15];
+      for (int k = 0; k < 32; k += 2) {
+        const e2 v = __builtin_convertvector(f32x2{scur[k >> 4][k & 15], scur[k >> 4][(k & 15) + 1]}, e2);
+        pb[k >> 3][k & 7] = v[0];
+        pb[k >> 3][(k & 7) + 1] = v[1];
+      }
     }
     // chunk cc of pb covers keys 16cc .. 16cc+15; its k-slots match V^T below.
 
@@ -490,7 +498,8 @@ void fwd_kernel(FwdParams p) {
   // wave is past the last tile) and written as whole rows; LSE = (mref +
   // log2 l) * ln 2.  A split writes its fp32 O and LSE for the combine pass.
   const float lt = pair_sum(l);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  // 1/l, times the dropout factor 1/(1-p) of the kept keys
+  const float inv = lt > 0.0f ? (DROPOUT ? p.drop_scale : 1.0f) / lt : 0.0f;
   const float lse_out = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
   if constexpr (SPLIT) {
     const size_t prow = ((size_t)split * p.heads + head) * N + qi;
