@@ -134,25 +134,34 @@ using Stage = std::integral_constant<int, S % 3>;
 // Keep bits of rows row0 .. row0+3 at this lane's key (bit e: row row0 + e),
 // for a lane whose quad (lanes 4m .. 4m+3) holds the keys 4m' .. 4m'+3 of one
 // Philox counter group (key & 3 == lane & 3).  Lane q draws the counter of row
-// row0 + q, whose four words are the four keys' draws at that row, and the
-// quad transposes the 4 x 4 words with DPP quad permutes: one Philox block per
-// lane for four elements instead of one per element.
+// row0 + q, whose four words are the four keys' draws at that row: one Philox
+// block per lane for four elements instead of one per element.  The quad then
+// transposes the 4 x 4 keep bits: lane q compares its words (bit i: key i at
+// row row0 + q) into nibble q of a 16-bit word, two DPP exchanges (lanes q^1,
+// then q^2) OR the four nibbles together in every lane, and lane q gathers
+// bits 4e + q (key q at row row0 + e) into bit e with one multiply.
 __device__ __forceinline__ uint32_t quad_keep4(const BwdParams& p, int row0, int key, int hi,
                                                int bi) {
   const int q = threadIdx.x & 3;
   const u32x4 w = philox((uint32_t)key >> 2, (uint32_t)(row0 + q), (uint32_t)hi, (uint32_t)(bi + p.b0),
                          p.seed_lo, p.seed_hi);
-  uint32_t bits = 0;
-  static_for<4>([&](auto j_t) {
-    constexpr int j = decltype(j_t)::value;
-    // Lane q reads lane (q + j) & 3, which sends word (sender - j) & 3 = q of
-    // its row's counter: this lane's key at row row0 + ((q + j) & 3).
-    const uint32_t send = philox_word(w, q - j);
-    constexpr int ctrl = (j & 3) | (((1 + j) & 3) << 2) | (((2 + j) & 3) << 4) | (((3 + j) & 3) << 6);
-    const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, ctrl, 0xF, 0xF, false);
-    bits |= (uint32_t)(got >= p.drop_threshold) << ((q + j) & 3);
-  });
-  return bits;
+  uint32_t kb = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kb |= (uint32_t)(w[i] >= p.drop_threshold) << i;
+  uint32_t m = kb << (4 * q);
+  constexpr int kXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // lane i reads lane i ^ 1 of its quad
+  constexpr int kXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);  // lane i reads lane i ^ 2
+  m |= (uint32_t)__builtin_amdgcn_mov_dpp((int)m, kXor1, 0xF, 0xF, false);
+  m |= (uint32_t)__builtin_amdgcn_mov_dpp((int)m, kXor2, 0xF, 0xF, false);
+  // bits 0, 4, 8, 12 of x times 1 + 2^3 + 2^6 + 2^9 land on bits 9 .. 12
+  // (every other product bit falls elsewhere, without carries)
+  const uint32_t x = (m >> q) & 0x1111u;
+  return ((x * 0x249u) >> 9) & 0xFu;
+}
+
+// 0xFFFFFFFF if bit b of bits is set, else 0: keeps or clears a float's bits.
+__device__ __forceinline__ uint32_t bit_mask(uint32_t bits, int b) {
+  return (uint32_t)((int32_t)(bits << (31 - b)) >> 31);
 }
 
 // One wave per SIMD, each owning 32 keys of the block: their K and V rows
@@ -171,6 +180,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void bwd_dkdv_kernel(BwdParams p) {
   using C = KvCfg<D>;
   using V8 = typename Elem<E>::v8;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef E e2 __attribute__((ext_vector_type(2)));
   using V4 = typename Elem<E>::v4;
   constexpr int ES = 2;
   constexpr int BQ = C::BQ, NW = C::NW, TILE = C::TILE, BK = C::BK;
@@ -505,21 +516,24 @@ void bwd_dkdv_kernel(BwdParams p) {
                       const f32x4& l4, int lo, auto masked_t) {
     constexpr bool MASKED = decltype(masked_t)::value;
     const int a = k >> 4, r = k & 15, g = r >> 2, e = r & 3;
+    float pt[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       float pv = fast_exp2(fmaf(s[a][r + x], c2, -l4[e + x]));
       if constexpr (MASKED) pv = (32 * a + 8 * g + e + x) >= lo ? pv : 0.0f;
       pin(pv);
       s[a][r + x] = pv;
-      float pt = pv;
+      pt[x] = pv;
       if constexpr (DROPOUT) {
         // the keep bits of the group's four rows, drawn with the first pair
         if (e + x == 0) zn |= quad_keep4(p, it * BQ + 32 * a + 8 * g + 4 * hh, key, hi, bi) << k;
-        const bool keep = (zn >> (k + x)) & 1;
-        pt = keep ? pv : 0.0f;  // the factor 1/(1-p) goes to dV once, in the epilogue
+        // dropped: 0 (the factor 1/(1-p) of the kept goes to dV once, in the epilogue)
+        pt[x] = __uint_as_float(__float_as_uint(pv) & bit_mask(zn, k + x));
       }
-      pb[2 * a + (g >> 1)][4 * (g & 1) + e + x] = (E)pt;
     }
+    const e2 pp = __builtin_convertvector(f32x2{pt[0], pt[1]}, e2);  // one packed conversion
+    pb[2 * a + (g >> 1)][4 * (g & 1) + e] = pp[0];
+    pb[2 * a + (g >> 1)][4 * (g & 1) + e + 1] = pp[1];
     pin_v(pb[2 * a + (g >> 1)]);  // keep the work beside this MFMA
   };
   // Row-offset bound of the causal mask for tile `it` (see exp_pair).
@@ -527,12 +541,16 @@ void bwd_dkdv_kernel(BwdParams p) {
   // dS of element pair (k, k+1) of the current tile into dsb.
   auto ds_pair = [&](V8 (&dsb)[4], int k, const f32x4& d4) {
     const int a = k >> 4, r = k & 15, g = r >> 2, e = r & 3;
+    float ds[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       float dp = sdp[a][r + x];
-      if constexpr (DROPOUT) dp = ((zb >> (k + x)) & 1) ? dp * p.drop_scale : 0.0f;
-      dsb[2 * a + (g >> 1)][4 * (g & 1) + e + x] = (E)(sp[a][r + x] * (dp - d4[e + x]));
+      if constexpr (DROPOUT) dp = __uint_as_float(__float_as_uint(dp * p.drop_scale) & bit_mask(zb, k + x));
+      ds[x] = sp[a][r + x] * (dp - d4[e + x]);
     }
+    const e2 dd = __builtin_convertvector(f32x2{ds[0], ds[1]}, e2);  // one packed conversion
+    dsb[2 * a + (g >> 1)][4 * (g & 1) + e] = dd[0];
+    dsb[2 * a + (g >> 1)][4 * (g & 1) + e + 1] = dd[1];
     pin_v(dsb[2 * a + (g >> 1)]);  // keep the work beside this MFMA
   };
 
