@@ -332,10 +332,11 @@ def _window_v(N, d, wd, dtype=torch.bfloat16):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_dropout_mask_bit_exact_forward(causal):
+@pytest.mark.parametrize("d", [64, 128])
+def test_dropout_mask_bit_exact_forward(causal, d):
     # Q = K = 0 makes P uniform over the allowed keys; V = a one-hot window puts
     # P~[i, wd + k] into O[i, k], which is non-zero exactly when that element is kept.
-    B, H, N, d, p, seed = 2, 3, 320, 64, 0.1, 0x0123456789ABCDEF
+    B, H, N, p, seed = 2, 3, 320, 0.1, 0x0123456789ABCDEF
     key_lens = torch.tensor([N, 250], dtype=torch.int32)
     zero = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
     got = np.zeros((B, H, N, N), dtype=bool)
@@ -357,11 +358,12 @@ def test_dropout_mask_bit_exact_forward(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_dropout_mask_bit_exact_backward(causal):
+@pytest.mark.parametrize("d", [64, 128])
+def test_dropout_mask_bit_exact_backward(causal, d):
     # The dK/dV kernel's keep bits.  Q = K = 0 makes P uniform over the allowed
     # keys; dO_i = a one-hot window on i gives dV[j, k] = P~[wd + k, j]:
     # non-zero exactly where the kernel keeps the allowed element (wd + k, j).
-    B, H, N, d, p, seed = 2, 2, 256, 64, 0.25, 0x1122334455667788
+    B, H, N, p, seed = 2, 2, 256, 0.25, 0x1122334455667788
     key_lens = torch.tensor([N, 201], dtype=torch.int32)
     zero = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
     v = torch.randn(B, H, N, d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
@@ -386,7 +388,8 @@ def test_dropout_mask_bit_exact_backward(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_dropout_mask_bit_exact_dq_kernel(causal):
+@pytest.mark.parametrize("d", [64, 128])
+def test_dropout_mask_bit_exact_dq_kernel(causal, d):
     # The dQ kernel draws its own keep bits.  Q = 0 makes P uniform (1/L_i over
     # the L_i allowed keys of row i); dO_i = V_j = e_0 makes dO V^T = 1, so the
     # dropped-out dP is Z_ij and D_i = sum_j Z_ij / L_i; K = a one-hot window
@@ -394,7 +397,7 @@ def test_dropout_mask_bit_exact_dq_kernel(causal):
     #     dQ[i, k] = scale * (Z[i, wd+k] - D_i) / L_i,
     # positive where key wd+k is kept and negative where it is dropped, in every
     # row that has both, and exactly 0 where the key is masked.
-    B, H, N, d, p, seed = 2, 3, 320, 64, 0.1, 0x0123456789ABCDEF
+    B, H, N, p, seed = 2, 3, 320, 0.1, 0x0123456789ABCDEF
     key_lens = torch.tensor([N, 250], dtype=torch.int32)
     zero = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
     e0 = torch.zeros(B, H, N, d)
